@@ -1,0 +1,126 @@
+"""Workload table and seeded synthetic input generator.
+
+This module holds sizes, seeds and random draws only; none of the layer's
+arithmetic lives here.  The tests and the benchmark use it to feed the same
+inputs to the GPU library and to the CPU oracle.
+
+Shapes follow the packed text+audio+video sequence of "vLLM-Omni 上的 MiniMax H3"
+(Chinese translation of the vLLM blog post): §1 (one packed, jointly denoised
+sequence), §3.1 (58,758 valid tokens in a 58,816-token aligned buffer; 128-channel
+head projections against a 5,376-channel hidden state, i.e. 42 heads of 128).
+The pages carry no tensors, so inputs are bf16 N(0, 1) draws of those shapes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+NAN_BF16_BITS = 0x7FC0  # quiet NaN
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    heads: int
+    n_valid: int
+    seq_buf: int
+    segments: tuple = ()          # (text, audio, video) token counts, in packed order
+    head_dim: int = 128
+    eps: float = 1e-6
+    theta: float = 10000.0
+    # Tokens [0, n_1d) take 1-D RoPE; the rest (video) take 3-axis RoPE.
+    n_1d: int | None = None       # None: every valid token is 1-D
+    sections: tuple = (0, 0, 0)   # channel split (t, h, w) for 3-axis tokens
+    grid: tuple = (0, 0, 0)       # (T, H, W) token grid for 3-axis tokens
+    seed: int = 0
+    batch: int = 1
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def rope_n_1d(self) -> int:
+        return self.n_valid if self.n_1d is None else self.n_1d
+
+    @property
+    def flops(self) -> float:
+        """Attention FLOP of one call: two N x N x D products at 2 flop per MAC."""
+        return 4.0 * self.batch * self.n_valid * self.n_valid * self.head_dim * self.heads
+
+
+WORKLOADS = {
+    0: Workload("tiny_2h_1000of1024", heads=2, n_valid=1000, seq_buf=1024, seed=0),
+    1: Workload("mid_8h_8150of8192", heads=8, n_valid=8150, seq_buf=8192,
+                segments=(300, 1850, 6000), seed=1),
+    2: Workload("share_6h_58758of58816", heads=6, n_valid=58758, seq_buf=58816,
+                segments=(512, 5246, 53000), seed=2),
+    3: Workload("layer_42h_58758of58816", heads=42, n_valid=58758, seq_buf=58816,
+                segments=(512, 5246, 53000), seed=3),
+    4: Workload("long_42h_87500of87552", heads=42, n_valid=87500, seq_buf=87552,
+                segments=(512, 7800, 79188), n_1d=512 + 7800, sections=(32, 48, 48),
+                grid=(99, 12, 67), seed=4),
+}
+
+
+def tail_fill_bits(mode: str) -> int | None:
+    """bf16 bit pattern written into the buffer tail: 'nan', 'big' (+3.0e4),
+    'zero', or None (leave the N(0,1) draw in place)."""
+    return {"nan": NAN_BF16_BITS, "big": 0x46EA, "zero": 0x0000, None: None}[mode]
+
+
+def generate(w: Workload, tail: str | None = "nan", seed: int | None = None,
+             shape_override: dict | None = None) -> dict:
+    """Seeded bf16 inputs on the CPU.
+
+    Draw order from one ``torch.Generator`` seeded with ``seed`` (default
+    ``w.seed``): Q, K, V as fp32 N(0,1) of shape [B, S, H, D] cast to bf16
+    (round-to-nearest-even), then w_q = 1 + 0.1 * N(0,1) [D], then w_k likewise.
+    Rows [N, S) of Q, K and V are then overwritten with ``tail``.
+    """
+    B, S, H, D = w.batch, w.seq_buf, w.heads, w.head_dim
+    if shape_override:
+        B = shape_override.get("batch", B)
+        S = shape_override.get("seq_buf", S)
+        H = shape_override.get("heads", H)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    out = {}
+    for name in ("q", "k", "v"):
+        out[name] = torch.randn((B, S, H, D), generator=g, dtype=torch.float32).to(
+            torch.bfloat16)
+    for name in ("w_q", "w_k"):
+        out[name] = (1.0 + 0.1 * torch.randn((D,), generator=g, dtype=torch.float32)).to(
+            torch.bfloat16)
+    fill = tail_fill_bits(tail)
+    n_valid = [w.n_valid] * B
+    if fill is not None:
+        for name in ("q", "k", "v"):
+            bits = out[name].view(torch.int16)
+            for b in range(B):
+                bits[b, n_valid[b]:] = torch.tensor(fill, dtype=torch.int32).to(torch.int16)
+    out["n_valid"] = n_valid
+    return out
+
+
+def bits(t: torch.Tensor):
+    """Bit patterns of a CPU bf16 tensor as a numpy uint16 array (no copy of values)."""
+    return t.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def sample_rows(w: Workload, per_head: int, seed: int) -> "list[int]":
+    """Query rows to check: ``per_head`` rows drawn uniformly without replacement from
+    [0, N) with a fixed seed, plus rows 0 and N-1 and the first and last row of every
+    packed segment.  Returned sorted; the same set serves every head."""
+    import numpy as np
+
+    n = w.n_valid
+    rng = np.random.default_rng(seed)
+    k = min(per_head, n)
+    rows = set(rng.choice(n, size=k, replace=False).tolist()) if k > 0 else set()
+    if n > 0:
+        rows.update((0, n - 1))
+    start = 0
+    for seg in w.segments:
+        if seg > 0:
+            rows.update((start, start + seg - 1))
+        start += seg
+    return sorted(r for r in rows if 0 <= r < n)

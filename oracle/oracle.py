@@ -1,0 +1,205 @@
+"""ctypes wrapper of the fp64 CPU oracle (``h3_oracle.cpp``).
+
+TEST INFRASTRUCTURE ONLY.  Importable by the tests, the smoke check and the
+benchmark's CPU-baseline leg; the product package never imports it.
+
+Inputs are numpy ``uint16`` arrays holding bf16 bit patterns (the exact values
+the GPU path receives); outputs are numpy ``float64`` arrays.  The definitions
+and the page passages they follow are documented in ``h3_oracle.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "h3_oracle.cpp")
+_LIB = os.path.join(_HERE, "libh3oracle.so")
+
+# Plain -O3 (vectorises the independent per-key / per-channel loops); no
+# -ffast-math and no FMA contraction, so each product and sum is rounded as written.
+GXX_CMD = ["g++", "-O3", "-std=c++17", "-fPIC", "-shared", "-pthread",
+           "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", _LIB]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle shared library (idempotent unless ``force``)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+            os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "h3_oracle.h"))):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = GXX_CMD[:-1] + [tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class Rope(ctypes.Structure):
+    """Oracle-side rotary descriptor (mirrors ``h3o_rope``)."""
+    _fields_ = [("theta", ctypes.c_double), ("n_1d", ctypes.c_int64),
+                ("sections", ctypes.c_int32 * 3), ("grid_t", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32)]
+
+
+def make_rope(theta: float, n_1d: int, sections=(0, 0, 0), grid=(0, 0, 0)) -> Rope:
+    r = Rope()
+    r.theta = float(theta)
+    r.n_1d = int(n_1d)
+    for i in range(3):
+        r.sections[i] = int(sections[i])
+    r.grid_t, r.grid_h, r.grid_w = (int(g) for g in grid)
+    return r
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        D = ctypes.c_double
+        I = ctypes.c_int
+        _lib.h3o_widen_bf16.argtypes = [P, I64, P]
+        _lib.h3o_widen_bf16.restype = None
+        _lib.h3o_rmsnorm_row.argtypes = [P, P, I64, D, P]
+        _lib.h3o_rmsnorm_row.restype = None
+        _lib.h3o_rope_row.argtypes = [P, I64, I, P, P, D, P]
+        _lib.h3o_rope_row.restype = I
+        _lib.h3o_token_position.argtypes = [ctypes.POINTER(Rope), I64,
+                                            ctypes.POINTER(I), P]
+        _lib.h3o_token_position.restype = I
+        _lib.h3o_prologue.argtypes = [P, I64, I64, I64, I64, P, I64, D,
+                                      ctypes.POINTER(Rope), P, I64, I, P]
+        _lib.h3o_prologue.restype = I
+        _lib.h3o_attention.argtypes = [P, P, P, I64, I64, I64, I64, D, I, P]
+        _lib.h3o_attention.restype = I
+        _lib.h3o_attn_varlen.argtypes = [P, P, P, I64, I64, I64, I64, I64, D, P, I64,
+                                         I, P]
+        _lib.h3o_attn_varlen.restype = I
+        _lib.h3o_attn_layer.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, I64, D,
+                                        ctypes.POINTER(Rope), D, P, I64, I, P]
+        _lib.h3o_attn_layer.restype = I
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 inputs must be passed as uint16 bit patterns")
+    return a
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def widen_bf16(bits) -> np.ndarray:
+    b = _u16(bits)
+    out = np.empty(b.shape, dtype=np.float64)
+    lib().h3o_widen_bf16(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def rmsnorm_row(x, w, eps: float) -> np.ndarray:
+    x = _f64(x)
+    w = _f64(w)
+    assert x.ndim == 1 and w.shape == x.shape
+    y = np.empty_like(x)
+    lib().h3o_rmsnorm_row(_ptr(x), _ptr(w), x.size, float(eps), _ptr(y))
+    return y
+
+
+def rope_row(x, mode: int, pos, sections=(0, 0, 0), theta: float = 10000.0) -> np.ndarray:
+    x = _f64(x)
+    p = _f64(list(pos) + [0.0] * (3 - len(pos)))
+    s = np.ascontiguousarray(sections, dtype=np.int32)
+    y = np.empty_like(x)
+    _check(lib().h3o_rope_row(_ptr(x), x.size, int(mode), _ptr(p), _ptr(s), float(theta),
+                              _ptr(y)), "rope_row")
+    return y
+
+
+def token_position(rope: Rope, i: int):
+    mode = ctypes.c_int()
+    pos = np.zeros(3, dtype=np.float64)
+    _check(lib().h3o_token_position(ctypes.byref(rope), int(i), ctypes.byref(mode),
+                                    _ptr(pos)), "token_position")
+    return mode.value, pos
+
+
+def prologue(x_bits, n_valid: int, w_bits, eps: float, rope: Rope, rows,
+             w_head_stride: int = 0, threads: int | None = None) -> np.ndarray:
+    """RMSNorm + RoPE of tokens ``rows`` of ``x_bits`` [S, H, D] -> [n_rows, H, D]."""
+    x = _u16(x_bits)
+    S, H, D = x.shape
+    w = _u16(w_bits)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), dtype=np.float64)
+    _check(lib().h3o_prologue(_ptr(x), H, D, H * D, int(n_valid), _ptr(w),
+                              int(w_head_stride), float(eps), ctypes.byref(rope),
+                              _ptr(rows), rows.size, threads or default_threads(),
+                              _ptr(out)), "prologue")
+    return out
+
+
+def attention(q, k, v, scale: float, threads: int | None = None) -> np.ndarray:
+    """Softmax attention on fp64 operands: q [R, H, D], k/v [N, H, D] -> [R, H, D]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    R, H, D = q.shape
+    N = k.shape[0]
+    assert k.shape == (N, H, D) and v.shape == (N, H, D)
+    out = np.empty((R, H, D), dtype=np.float64)
+    _check(lib().h3o_attention(_ptr(q), _ptr(k), _ptr(v), R, N, H, D, float(scale),
+                               threads or default_threads(), _ptr(out)), "attention")
+    return out
+
+
+def attn_varlen(q_bits, k_bits, v_bits, n_valid: int, scale: float, rows,
+                threads: int | None = None) -> np.ndarray:
+    """Attention over bf16 [S, H, D] buffers (Q/K already prepared) -> [R, H, D]."""
+    q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
+    S, H, D = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), dtype=np.float64)
+    _check(lib().h3o_attn_varlen(_ptr(q), _ptr(k), _ptr(v), S, int(n_valid), H, D, H * D,
+                                 float(scale), _ptr(rows), rows.size,
+                                 threads or default_threads(), _ptr(out)), "attn_varlen")
+    return out
+
+
+def attn_layer(q_bits, k_bits, v_bits, n_valid: int, wq_bits, wk_bits, eps: float,
+               rope: Rope, scale: float, rows, w_head_stride: int = 0,
+               threads: int | None = None) -> np.ndarray:
+    """RMSNorm + RoPE + attention over bf16 [S, H, D] buffers -> [R, H, D]."""
+    q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
+    wq, wk = _u16(wq_bits), _u16(wk_bits)
+    S, H, D = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), dtype=np.float64)
+    _check(lib().h3o_attn_layer(_ptr(q), _ptr(k), _ptr(v), S, int(n_valid), H, D, H * D,
+                                _ptr(wq), _ptr(wk), int(w_head_stride), float(eps),
+                                ctypes.byref(rope), float(scale), _ptr(rows), rows.size,
+                                threads or default_threads(), _ptr(out)), "attn_layer")
+    return out
