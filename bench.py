@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of libh3attn on one MI355X.
+
+One step = one h3_attn_layer call (K/V pre-pass + attention with the fused Q
+prologue) over the 42-head x 58,758-valid-token packed buffer (58,816 rows) with
+inputs already resident in HBM.  Prints one JSON line:
+
+  value      attention TFLOP/s of the whole step, FLOP = 4 * N^2 * D * H
+  roofline   the dominant kernel (attention, timed alone via h3_attn_packed with HIP
+             events on the launch stream) against the bf16 dense MFMA peak
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload
+             (sampled query rows of every head), whose rows also gate parity
+  kernels    the other kernels' achieved bandwidth (K/V pre-pass, standalone prologue)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s + % bf16 MFMA peak, 42 heads x 58,758 valid tokens, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+KERNEL_SOURCES = ("long_sequence_attention_h3_amd/csrc/attention.hpp",
+                  "long_sequence_attention_h3_amd/csrc/common.hpp",
+                  "long_sequence_attention_h3_amd/csrc/prologue.hpp",
+                  "long_sequence_attention_h3_amd/csrc/h3attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_units: float):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--cpu-rows-per-head", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the layer is "
+              "measured on one GPU's share; multi-GPU sharding is not part of this build.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from long_sequence_attention_h3_amd import binding as B
+    from long_sequence_attention_h3_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    log(f"[bench] workload {args.workload} {w.name}: H={w.heads} N={w.n_valid} S={w.seq_buf}")
+    t0 = time.time()
+    inp = W.generate(w, tail="nan")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+    rope = B.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    n = d["n_valid"]
+    out = torch.empty_like(d["q"])
+    ws = torch.empty(B.workspace_size(d["q"]), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        B.attn_layer(d["q"], d["k"], d["v"], d["w_q"], d["w_k"], n, w.eps, rope, scale,
+                     out=out, workspace=ws)
+
+    # ---- headline: K whole-layer steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    flops = w.flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] h3_attn_layer {ms_step:.3f} ms/step  {value:.1f} TFLOP/s "
+        f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), wall {wall:.3f}s")
+    layer_out = out.clone()
+
+    # ---- dominant kernel alone: attention from packed K/V (fused Q prologue)
+    B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps, rope=rope)
+    for _ in range(2):
+        B.attn_packed(d["q"], ws, n, scale, w_q=d["w_q"], eps=w.eps, rope=rope, out=out)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        B.attn_packed(d["q"], ws, n, scale, w_q=d["w_q"], eps=w.eps, rope=rope, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn = e0.elapsed_time(e1) / args.steps
+    achieved = flops / (ms_attn * 1e-3) / 1e12
+    assert torch.equal(out.view(torch.int16), layer_out.view(torch.int16)), \
+        "two-stage call differs from h3_attn_layer"
+    log(f"[bench] attention kernel {ms_attn:.3f} ms  {achieved:.1f} TFLOP/s")
+
+    # ---- other kernels: K/V pre-pass and the standalone prologue (HBM-bound)
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    row_bytes = w.heads * w.head_dim * 2
+    tiles = (w.n_valid + 63) // 64
+    pack_bytes = 2 * w.n_valid * row_bytes + 2 * w.heads * tiles * 16384
+    ms_pack = timed(lambda: B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps,
+                                      rope=rope), args.steps)
+    q2, k2 = torch.empty_like(d["q"]), torch.empty_like(d["k"])
+    prol_bytes = 2 * 2 * w.n_valid * row_bytes
+    ms_prol = timed(lambda: B.qk_rmsnorm_rope(d["q"], d["k"], d["w_q"], d["w_k"], n, w.eps,
+                                              rope, q_out=q2, k_out=k2), args.steps)
+    log(f"[bench] kv_pack {ms_pack:.3f} ms ({pack_bytes / ms_pack / 1e6:.0f} GB/s), "
+        f"qk_rmsnorm_rope {ms_prol:.3f} ms ({prol_bytes / ms_prol / 1e6:.0f} GB/s)")
+
+    traffic = measured_traffic(1.0)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim,
+                   "n_valid": w.n_valid, "seq_buf": w.seq_buf, "batch": w.batch,
+                   "entry": "h3_attn_layer", "rope": "1-D" if w.n_1d is None else "1-D+3-axis",
+                   "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd_kernel",
+                     "kernel_ms": round(ms_attn, 4)},
+        "kernels": {
+            "kv_pack_kernel": {"ms": round(ms_pack, 4), "bytes": pack_bytes,
+                               "GB/s": round(pack_bytes / ms_pack / 1e6, 1),
+                               "frac_hbm": round(pack_bytes / ms_pack / 1e6 / PEAK_HBM_GBS, 4)},
+            "qk_norm_rope_kernel": {"ms": round(ms_prol, 4), "bytes": prol_bytes,
+                                    "GB/s": round(prol_bytes / ms_prol / 1e6, 1),
+                                    "frac_hbm": round(prol_bytes / ms_prol / 1e6 /
+                                                      PEAK_HBM_GBS, 4)},
+        },
+        "wall_s_timed_region": round(wall, 4),
+        "source_hash": source_hash(),
+    }
+
+    # ---- CPU baseline: the fp64 oracle on sampled rows of every head
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        rows = W.sample_rows(w, args.cpu_rows_per_head, 30_000 + args.workload)
+        threads = O.default_threads()
+        orope = O.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
+        log(f"[bench] oracle on {len(rows)} rows x {w.heads} heads, {threads} threads")
+        t0 = time.perf_counter()
+        ref = O.attn_layer(W.bits(inp["q"][0]), W.bits(inp["k"][0]), W.bits(inp["v"][0]),
+                           w.n_valid, W.bits(inp["w_q"]), W.bits(inp["w_k"]), w.eps, orope,
+                           scale, np.asarray(rows, dtype=np.int64), threads=threads)
+        t_cpu = time.perf_counter() - t0
+        cpu_flops = 4.0 * len(rows) * w.n_valid * w.head_dim * w.heads
+        idx = torch.as_tensor(rows, dtype=torch.long, device=dev)
+        got = layer_out[0].index_select(0, idx).float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        parity_ok = bool(err.max() <= 1.5e-2 and err.mean() <= 2e-3 and rel <= 1e-2)
+        log(f"[bench] oracle {t_cpu:.1f}s; parity max {err.max():.2e} mean {err.mean():.2e} "
+            f"relL2 {rel:.2e} -> {'ok' if parity_ok else 'FAIL'}")
+        result["cpu_baseline"] = {
+            "value": round(cpu_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} sampled query rows x {w.heads} heads of {w.name} "
+                      f"(all {w.n_valid} keys each), fp64, {t_cpu:.1f} s",
+            "seconds": round(t_cpu, 2), "cpu_model": cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "gpu_over_cpu": round(value / (cpu_flops / t_cpu / 1e12), 1),
+        }
+        result["parity"] = {"rows": len(rows), "max_abs": float(err.max()),
+                            "mean_abs": float(err.mean()), "rel_l2": rel, "ok": parity_ok}
+        if not parity_ok:
+            print(json.dumps(result), flush=True)
+            log("[bench] parity FAILED against the oracle")
+            return 1
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

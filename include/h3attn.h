@@ -1,0 +1,161 @@
+/*
+ * h3attn.h — C ABI of libh3attn: the self-attention layer of a joint audio/video
+ * DiT over a packed text+audio+video token sequence, on AMD MI355X (gfx950).
+ *
+ * Pages cited:
+ *   [Blog] "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH3 的实时服务"
+ *          (Chinese translation of the vLLM blog post on serving MiniMax H3).
+ *     §1    text, audio and video tokens form one packed sequence, denoised jointly;
+ *     §3.1  "长序列注意力与通信": the packed sequence sits in an aligned buffer
+ *           (58,758 valid tokens of 58,816); attention receives the valid length and
+ *           the structural tail padding is dropped; RoPE rows are built per token;
+ *           heads are 128-channel projections of a 5,376-channel hidden state;
+ *     §3.2  "融合的 DiT 算子": Q/K RMSNorm and RoPE are one fused operator;
+ *     §3.5  speed-ups are "lossless" but not bitwise identical to other kernels.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ *
+ *  - Tensors are bf16, in caller-owned DEVICE memory, laid out [B, S, H, D]:
+ *    token t of batch b, head h, channel c at  base + b*S*stride + t*stride + h*D + c
+ *    (element offsets), where stride is the row stride in elements (>= H*D; a fused
+ *    [S, 3, H, D] QKV buffer is addressed with stride 3*H*D).
+ *  - Only D = 128 is supported.  Every pointer and every row stride must be
+ *    16-byte aligned (stride a multiple of 8 elements).
+ *  - Rows [N_b, S) of every input may hold anything, NaN included; they never
+ *    enter the arithmetic.  Output rows [N_b, S) of an attention call are written
+ *    as exact zeros.  N_b = 0 is valid.
+ *  - All work is enqueued asynchronously on `stream` (NULL: the default stream).
+ *    The status reports argument validation and launch errors only; faults on the
+ *    device surface at the caller's next synchronisation.  Nothing is allocated
+ *    on the device: the attention calls take a caller-provided workspace.
+ *  - No state is kept between calls; calls on different streams are independent
+ *    as long as their output and workspace buffers do not overlap.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  H3_OK = 0,
+  H3_ERR_NULL = 1,         /* a required pointer is NULL                            */
+  H3_ERR_SHAPE = 2,        /* inconsistent sizes (N > S, N < 0, stride < H*D, ...)  */
+  H3_ERR_ALIGN = 3,        /* pointer or stride not 16-byte aligned                 */
+  H3_ERR_UNSUPPORTED = 4,  /* head_dim != 128, bad RoPE sections or grid            */
+  H3_ERR_DEVICE = 5,       /* no current HIP device, or it is not gfx950            */
+  H3_ERR_LAUNCH = 6,       /* a kernel launch failed                                */
+  H3_ERR_WORKSPACE = 7     /* workspace missing or smaller than h3_attn_workspace_size */
+} h3_status;
+
+/* One packed, aligned buffer ([Blog §3.1]: a valid length inside an aligned buffer). */
+typedef struct {
+  int32_t batch;             /* B >= 1                                              */
+  int32_t num_heads;         /* H >= 1                                              */
+  int32_t head_dim;          /* D; must be 128                                      */
+  int64_t seq_buf;           /* S: rows allocated per sequence                      */
+  const int64_t* seq_valid;  /* HOST array [B]: N_b, 0 <= N_b <= S                  */
+  int64_t in_row_stride;     /* row stride (elements) of Q, K, V and prologue inputs */
+  int64_t out_row_stride;    /* row stride (elements) of O and prologue outputs      */
+} h3_shape;
+
+/* Rotary descriptor: the per-token "RoPE rows" of [Blog §3.1].
+ * Tokens t < n_1d rotate as 1-D RoPE at position t over all D channels: pairs
+ * (j, j + D/2), angle t * theta^(-2j/D).  Tokens t >= n_1d (video) rotate as 3-axis
+ * RoPE: k = t - n_1d, (pt, ph, pw) = (k / (gh*gw), (k / gw) % gh, k % gw); channel
+ * sections of sizes sections[0..2] at offsets 0, s0, s0+s1 rotate by pt, ph, pw,
+ * pairs (off + j, off + j + s/2), angle p * theta^(-2j/s).  When every valid token is
+ * 1-D (n_1d >= N) the sections and grid are ignored; otherwise each section size must
+ * be even and positive with s0 + s1 + s2 = D, and the grid must hold N - n_1d tokens. */
+typedef struct {
+  double theta;              /* base, e.g. 10000                                    */
+  int64_t n_1d;
+  int32_t sections[3];       /* e.g. {32, 48, 48}                                   */
+  int32_t grid_t, grid_h, grid_w;
+} h3_rope;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* h3_status_string(h3_status s);
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int h3_version(void);
+
+/* Fused per-head Q/K RMSNorm + RoPE  ([Blog §3.2]).
+ * For every valid token t < N_b and head h, independently for X in {Q, K}:
+ *   y = x / sqrt(mean_c x_c^2 + eps) * w[h*w_head_stride + c]   (fp32 arithmetic)
+ *   out = RoPE_t(y)   (descriptor above), rounded to bf16 (nearest even).
+ * q_in/k_in are read with in_row_stride, q_out/k_out written with out_row_stride.
+ * Output rows [N_b, S) are left untouched.  In place (q_out == q_in, equal strides)
+ * is allowed; partially overlapping buffers are not.
+ * w_q, w_k: bf16 device arrays, [D] when w_head_stride == 0, [H][w_head_stride] else.
+ * Errors: H3_ERR_NULL, H3_ERR_SHAPE, H3_ERR_ALIGN, H3_ERR_UNSUPPORTED, H3_ERR_DEVICE,
+ * H3_ERR_LAUNCH. */
+h3_status h3_qk_rmsnorm_rope(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                             const void* w_q, const void* w_k, int64_t w_head_stride,
+                             float eps, const h3_rope* rope, const h3_shape* shape,
+                             hipStream_t stream);
+
+/* Bytes of device workspace an attention call with this shape needs (0 if the shape
+ * is invalid).  The workspace holds the key and value operands of every batch repacked
+ * for the attention kernel: B * 2 * H * round_up(S, 64) * D bf16 values. */
+size_t h3_attn_workspace_size(const h3_shape* shape);
+
+/* Stage 1 of attention: repack K and V of every batch into `workspace` (keys of 64-key
+ * tiles as the attention kernel reads them; keys >= N_b stored as zeros).  With w_k
+ * non-NULL each K row is first RMS-normalised (weights w_k, w_head_stride, eps) and
+ * rotated (rope), exactly as h3_qk_rmsnorm_rope does; with w_k NULL, K is used as is
+ * and rope/eps are ignored.  Reads K and V with in_row_stride.  The packed workspace
+ * stays valid for any number of h3_attn_packed calls with the same shape.
+ * Errors: H3_ERR_NULL, H3_ERR_SHAPE, H3_ERR_ALIGN, H3_ERR_UNSUPPORTED, H3_ERR_DEVICE,
+ * H3_ERR_LAUNCH, H3_ERR_WORKSPACE. */
+h3_status h3_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
+                     float eps, const h3_rope* rope, const h3_shape* shape, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 2 of attention: O = softmax(scale * Q K^T) V over the valid keys, with K and V
+ * taken from a workspace filled by h3_kv_pack for the same shape.  With w_q non-NULL
+ * each Q row is RMS-normalised and rotated in registers on load (same arithmetic as
+ * h3_qk_rmsnorm_rope); with w_q NULL, Q is used as is.  Output rows [N_b, S) are zero.
+ * Errors: as h3_kv_pack. */
+h3_status h3_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head_stride,
+                         float eps, const h3_rope* rope, float softmax_scale,
+                         const h3_shape* shape, const void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Dense non-causal softmax attention over the valid tokens ([Blog §3.1]), with Q and
+ * K already normalised and rotated:
+ *   O[t, h, :] = sum_{j<N} softmax_j(scale * Q[t,h,:] . K[j,h,:]) V[j, h, :]   t < N
+ *   O[t, h, :] = 0                                                           N <= t < S
+ * Products in bf16 on the matrix cores with fp32 accumulation; softmax in fp32;
+ * output rounded to bf16.  The result is deterministic run to run.  Equivalent to
+ * h3_kv_pack (w_k NULL) followed by h3_attn_packed (w_q NULL).
+ * workspace: device buffer of at least h3_attn_workspace_size(shape) bytes, 256-byte
+ * aligned, not shared with a concurrent call.
+ * Errors: as h3_qk_rmsnorm_rope, plus H3_ERR_WORKSPACE. */
+h3_status h3_attn_varlen(const void* q, const void* k, const void* v, void* o,
+                         float softmax_scale, const h3_shape* shape, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* The whole layer: per-head Q/K RMSNorm + RoPE fused into the attention prologue,
+ * then attention as in h3_attn_varlen.  Bit-identical to h3_qk_rmsnorm_rope followed
+ * by h3_attn_varlen, but normalised Q and K never round-trip through a bf16 [S, H, D]
+ * buffer: K is prepared once into the workspace (h3_kv_pack with w_k), Q in registers
+ * (h3_attn_packed with w_q).  Inputs are not modified.
+ * Errors: as h3_attn_varlen. */
+h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
+                        const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
+                        const h3_rope* rope, float softmax_scale, const h3_shape* shape,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H */

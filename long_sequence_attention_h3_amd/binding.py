@@ -1,0 +1,252 @@
+"""Thin ctypes binding of libh3attn (include/h3attn.h).
+
+Argument marshalling only: torch supplies device memory and the current stream,
+every step of the layer runs in the library's HIP kernels.  There is no CPU or
+PyTorch fallback: if ``libh3attn.so`` is missing or the device is not a gfx950,
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libh3attn.so")
+
+H3_OK = 0
+STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_NULL", 2: "H3_ERR_SHAPE", 3: "H3_ERR_ALIGN",
+                4: "H3_ERR_UNSUPPORTED", 5: "H3_ERR_DEVICE", 6: "H3_ERR_LAUNCH",
+                7: "H3_ERR_WORKSPACE"}
+
+
+class H3Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    """``h3_shape``."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("seq_buf", ctypes.c_int64),
+                ("seq_valid", ctypes.POINTER(ctypes.c_int64)),
+                ("in_row_stride", ctypes.c_int64), ("out_row_stride", ctypes.c_int64)]
+
+
+class Rope(ctypes.Structure):
+    """``h3_rope``."""
+    _fields_ = [("theta", ctypes.c_double), ("n_1d", ctypes.c_int64),
+                ("sections", ctypes.c_int32 * 3), ("grid_t", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32)]
+
+
+def make_rope(theta: float, n_1d: int, sections=(0, 0, 0), grid=(0, 0, 0)) -> Rope:
+    r = Rope()
+    r.theta = float(theta)
+    r.n_1d = int(n_1d)
+    for i in range(3):
+        r.sections[i] = int(sections[i])
+    r.grid_t, r.grid_h, r.grid_w = (int(g) for g in grid)
+    return r
+
+
+EXPORTED = ("h3_status_string", "h3_version", "h3_qk_rmsnorm_rope", "h3_attn_workspace_size",
+            "h3_kv_pack", "h3_attn_packed", "h3_attn_varlen", "h3_attn_layer")
+
+_lib = None
+
+
+def lib():
+    """Load libh3attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing; build it with "
+                "`python -m long_sequence_attention_h3_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        SH, RP = ctypes.POINTER(Shape), ctypes.POINTER(Rope)
+        L.h3_status_string.argtypes = [ctypes.c_int]
+        L.h3_status_string.restype = ctypes.c_char_p
+        L.h3_version.argtypes = []
+        L.h3_version.restype = ctypes.c_int
+        L.h3_qk_rmsnorm_rope.argtypes = [P, P, P, P, P, P, I64, F, RP, SH, P]
+        L.h3_qk_rmsnorm_rope.restype = ctypes.c_int
+        L.h3_attn_workspace_size.argtypes = [SH]
+        L.h3_attn_workspace_size.restype = SZ
+        L.h3_kv_pack.argtypes = [P, P, P, I64, F, RP, SH, P, SZ, P]
+        L.h3_kv_pack.restype = ctypes.c_int
+        L.h3_attn_packed.argtypes = [P, P, P, I64, F, RP, F, SH, P, SZ, P]
+        L.h3_attn_packed.restype = ctypes.c_int
+        L.h3_attn_varlen.argtypes = [P, P, P, P, F, SH, P, SZ, P]
+        L.h3_attn_varlen.restype = ctypes.c_int
+        L.h3_attn_layer.argtypes = [P, P, P, P, P, P, I64, F, RP, F, SH, P, SZ, P]
+        L.h3_attn_layer.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != H3_OK:
+        msg = lib().h3_status_string(status).decode()
+        raise H3Error(status, f"{what}: {msg}")
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    """Row stride (elements) of a [B, S, H, D] or [S, H, D] bf16 device tensor whose heads
+    and channels are packed and whose batches are S rows apart."""
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() == 3:
+        t = t.unsqueeze(0)
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, S, H, D] or [S, H, D]")
+    B, S, H, D = t.shape
+    if t.stride(3) != 1 or t.stride(2) != D:
+        raise ValueError(f"{name}: heads and channels must be packed")
+    if B > 1 and t.stride(0) != S * t.stride(1):
+        raise ValueError(f"{name}: batches must be S rows apart")
+    return t.stride(1)
+
+
+def _dims(t: torch.Tensor):
+    return (1, *t.shape) if t.dim() == 3 else tuple(t.shape)
+
+
+class _Call:
+    """Holds ctypes objects alive for the duration of a call."""
+
+    def __init__(self, x: torch.Tensor, n_valid, in_stride: int, out_stride: int):
+        B, S, H, D = _dims(x)
+        if isinstance(n_valid, int):
+            n_valid = [n_valid] * B
+        if len(n_valid) != B:
+            raise ValueError("n_valid must have one entry per batch")
+        self.valid = (ctypes.c_int64 * B)(*[int(n) for n in n_valid])
+        self.shape = Shape(B, H, D, S, ctypes.cast(self.valid, ctypes.POINTER(ctypes.c_int64)),
+                           in_stride, out_stride)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def workspace_size(x: torch.Tensor) -> int:
+    """Workspace bytes an attention call on a tensor shaped like ``x`` needs."""
+    c = _Call(x, 0, x.shape[-2] * x.shape[-1], x.shape[-2] * x.shape[-1])
+    return int(lib().h3_attn_workspace_size(ctypes.byref(c.shape)))
+
+
+def _workspace(q: torch.Tensor, call: _Call, workspace):
+    need = int(lib().h3_attn_workspace_size(ctypes.byref(call.shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    return workspace
+
+
+def qk_rmsnorm_rope(q, k, w_q, w_k, n_valid, eps: float, rope: Rope, q_out=None,
+                    k_out=None, stream=None):
+    """Fused per-head Q/K RMSNorm + RoPE (h3_qk_rmsnorm_rope).  Returns (q_out, k_out);
+    pass ``q_out=q, k_out=k`` to work in place.  Output rows [N, S) are not written."""
+    s_in = _row_stride(q, "q")
+    if _row_stride(k, "k") != s_in:
+        raise ValueError("q and k must share a row stride")
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    k_out = torch.empty_like(k) if k_out is None else k_out
+    s_out = _row_stride(q_out, "q_out")
+    if _row_stride(k_out, "k_out") != s_out:
+        raise ValueError("q_out and k_out must share a row stride")
+    H = q.shape[-2]
+    w_head_stride = 0 if w_q.dim() == 1 else w_q.stride(0)
+    call = _Call(q, n_valid, s_in, s_out)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_qk_rmsnorm_rope(_p(q), _p(k), _p(q_out), _p(k_out), _p(w_q), _p(w_k),
+                                    w_head_stride, float(eps), ctypes.byref(rope),
+                                    ctypes.byref(call.shape), ctypes.c_void_p(st)),
+           "h3_qk_rmsnorm_rope")
+    return q_out, k_out
+
+
+def attn_varlen(q, k, v, n_valid, softmax_scale: float, out=None, workspace=None,
+                stream=None):
+    """Attention over the valid tokens with pre-normalised, pre-rotated Q/K
+    (h3_attn_varlen).  Output rows [N, S) are zero."""
+    s_in = _row_stride(q, "q")
+    for name, t in (("k", k), ("v", v)):
+        if _row_stride(t, name) != s_in:
+            raise ValueError("q, k and v must share a row stride")
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    s_out = _row_stride(out, "out")
+    call = _Call(q, n_valid, s_in, s_out)
+    ws = _workspace(q, call, workspace)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_varlen(_p(q), _p(k), _p(v), _p(out), float(softmax_scale),
+                                ctypes.byref(call.shape), _p(ws), ws.numel(),
+                                ctypes.c_void_p(st)), "h3_attn_varlen")
+    return out
+
+
+def attn_layer(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_scale: float,
+               out=None, workspace=None, stream=None):
+    """The whole layer: Q/K RMSNorm + RoPE fused into attention (h3_attn_layer)."""
+    s_in = _row_stride(q, "q")
+    for name, t in (("k", k), ("v", v)):
+        if _row_stride(t, name) != s_in:
+            raise ValueError("q, k and v must share a row stride")
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    s_out = _row_stride(out, "out")
+    w_head_stride = 0 if w_q.dim() == 1 else w_q.stride(0)
+    call = _Call(q, n_valid, s_in, s_out)
+    ws = _workspace(q, call, workspace)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_layer(_p(q), _p(k), _p(v), _p(out), _p(w_q), _p(w_k), w_head_stride,
+                               float(eps), ctypes.byref(rope), float(softmax_scale),
+                               ctypes.byref(call.shape), _p(ws), ws.numel(),
+                               ctypes.c_void_p(st)), "h3_attn_layer")
+    return out
+
+
+def kv_pack(k, v, n_valid, workspace=None, w_k=None, eps: float = 0.0, rope: Rope | None = None,
+            stream=None):
+    """Stage 1 (h3_kv_pack): repack K (normalised + rotated when ``w_k`` is given) and V
+    into a workspace for h3_attn_packed.  Returns the workspace."""
+    s_in = _row_stride(k, "k")
+    if _row_stride(v, "v") != s_in:
+        raise ValueError("k and v must share a row stride")
+    call = _Call(k, n_valid, s_in, s_in)
+    ws = _workspace(k, call, workspace)
+    w_head_stride = 0 if (w_k is None or w_k.dim() == 1) else w_k.stride(0)
+    st = _stream(k.device) if stream is None else stream
+    _check(lib().h3_kv_pack(_p(k), _p(v), _p(w_k), w_head_stride, float(eps),
+                            ctypes.byref(rope) if rope is not None else None,
+                            ctypes.byref(call.shape), _p(ws), ws.numel(), ctypes.c_void_p(st)),
+           "h3_kv_pack")
+    return ws
+
+
+def attn_packed(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: float = 0.0,
+                rope: Rope | None = None, out=None, stream=None):
+    """Stage 2 (h3_attn_packed): attention of ``q`` (normalised + rotated in registers when
+    ``w_q`` is given) against K/V packed by ``kv_pack``."""
+    s_in = _row_stride(q, "q")
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    s_out = _row_stride(out, "out")
+    call = _Call(q, n_valid, s_in, s_out)
+    w_head_stride = 0 if (w_q is None or w_q.dim() == 1) else w_q.stride(0)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_packed(_p(q), _p(out), _p(w_q), w_head_stride, float(eps),
+                                ctypes.byref(rope) if rope is not None else None,
+                                float(softmax_scale), ctypes.byref(call.shape), _p(workspace),
+                                workspace.numel(), ctypes.c_void_p(st)), "h3_attn_packed")
+    return out

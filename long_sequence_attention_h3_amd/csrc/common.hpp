@@ -1,0 +1,86 @@
+// common.hpp — types and small device helpers shared by the libh3attn kernels
+// (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kHeadDim = 128;        // the only supported head size
+constexpr int kChunks = kHeadDim / 8;  // 16-byte chunks (8 bf16) per head row
+constexpr int kTileKeys = 64;        // keys per packed K/V tile
+constexpr int kTileBytes = kTileKeys * kHeadDim * 2;  // 16 KiB per tile image
+
+// Rotary descriptor as the kernels see it.
+struct RopeArgs {
+  double theta;
+  int64_t n_1d;       // tokens [0, n_1d) are 1-D
+  int32_t sec[3];     // 3-axis channel sections (multiples of 16)
+  int32_t gt, gh, gw;
+};
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even.
+__device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ void unpack8(u32x4 raw, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w = raw[i];
+    f[2 * i] = __uint_as_float(w << 16);
+    f[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return r;
+}
+
+// Value of x held by lane (l ^ 32), via v_permlane32_swap.
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                            false);
+  // lanes 0-31 receive the upper half in r[1]; lanes 32-63 the lower half in r[0]
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// max / sum of x over the lane pair (l, l ^ 32); identical bits in both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                            false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                            false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup -> logical tile.  Consecutive workgroup ids are dispatched round-robin over
+// the 8 XCDs; this bijection hands each XCD one contiguous range of logical tiles, so
+// the workgroups resident on one XCD (sharing its L2) work on the same head.
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  constexpr int kXcd = 8;
+  const int per = total / kXcd, rem = total % kXcd;
+  const int xcd = pid % kXcd, idx = pid / kXcd;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+}  // namespace h3

@@ -1,0 +1,336 @@
+// h3attn.hip — libh3attn: C ABI entry points (declared in include/h3attn.h), argument
+// validation and kernel launches.  Kernels live in prologue.hpp and attention.hpp.
+//
+// Pages: "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH3 的实时服务"
+// (Chinese translation of the vLLM blog post), §3.1 (valid-length attention over an
+// aligned packed buffer, per-token RoPE rows) and §3.2 (fused Q/K RMSNorm + RoPE).
+#include "h3attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "attention.hpp"
+#include "prologue.hpp"
+
+#ifndef H3_ROWS_PER_WAVE_BLOCKS
+#define H3_ROWS_PER_WAVE_BLOCKS 1  // 32-row blocks of queries per wave
+#endif
+
+namespace {
+
+using namespace h3;
+
+constexpr int kRB = H3_ROWS_PER_WAVE_BLOCKS;
+constexpr int kBM = 4 * 32 * kRB;  // query rows per attention workgroup
+
+// ---------------------------------------------------------------- device check
+// Per-device verdict of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+h3_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return H3_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (v == 1) return H3_OK;
+    if (v == 2) return H3_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return H3_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? H3_OK : H3_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------- validation
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+h3_status check_shape(const h3_shape* s, int64_t* max_valid) {
+  if (!s || !s->seq_valid) return H3_ERR_NULL;
+  if (s->batch < 1 || s->num_heads < 1 || s->seq_buf < 0) return H3_ERR_SHAPE;
+  if (s->head_dim != kHeadDim) return H3_ERR_UNSUPPORTED;
+  const int64_t hd = (int64_t)s->num_heads * kHeadDim;
+  if (s->in_row_stride < hd || s->out_row_stride < hd) return H3_ERR_SHAPE;
+  if ((s->in_row_stride % 8) != 0 || (s->out_row_stride % 8) != 0) return H3_ERR_ALIGN;
+  // the grids index rows and heads with 32-bit block ids
+  if (s->seq_buf > (int64_t)1 << 30 || s->num_heads > (1 << 16)) return H3_ERR_SHAPE;
+  int64_t mx = 0;
+  for (int b = 0; b < s->batch; ++b) {
+    const int64_t n = s->seq_valid[b];
+    if (n < 0 || n > s->seq_buf) return H3_ERR_SHAPE;
+    if (n > mx) mx = n;
+  }
+  *max_valid = mx;
+  return H3_OK;
+}
+
+h3_status check_rope(const h3_rope* r, int64_t max_valid, RopeArgs* out) {
+  if (!r) return H3_ERR_NULL;
+  if (!(r->theta > 0.0) || !std::isfinite(r->theta) || r->n_1d < 0) return H3_ERR_UNSUPPORTED;
+  out->theta = r->theta;
+  out->n_1d = r->n_1d;
+  for (int i = 0; i < 3; ++i) out->sec[i] = r->sections[i];
+  out->gt = r->grid_t;
+  out->gh = r->grid_h;
+  out->gw = r->grid_w;
+  if (max_valid <= r->n_1d) {  // every valid token is 1-D
+    out->sec[0] = out->sec[1] = out->sec[2] = 0;
+    out->gt = out->gh = out->gw = 1;
+    return H3_OK;
+  }
+  int sum = 0;
+  for (int i = 0; i < 3; ++i) {
+    // each 8-channel chunk must sit inside one half of one section
+    if (r->sections[i] <= 0 || (r->sections[i] % 16) != 0) return H3_ERR_UNSUPPORTED;
+    sum += r->sections[i];
+  }
+  if (sum != kHeadDim) return H3_ERR_UNSUPPORTED;
+  if (r->grid_t <= 0 || r->grid_h <= 0 || r->grid_w <= 0) return H3_ERR_UNSUPPORTED;
+  const int64_t cells = (int64_t)r->grid_t * r->grid_h * r->grid_w;
+  if (max_valid - r->n_1d > cells) return H3_ERR_UNSUPPORTED;
+  return H3_OK;
+}
+
+h3_status check_weights(const void* w_q, const void* w_k, int64_t w_head_stride) {
+  if (!w_q || !w_k) return H3_ERR_NULL;
+  if (!aligned16(w_q) || !aligned16(w_k)) return H3_ERR_ALIGN;
+  if (w_head_stride != 0 && w_head_stride < kHeadDim) return H3_ERR_SHAPE;
+  if ((w_head_stride % 8) != 0) return H3_ERR_ALIGN;
+  return H3_OK;
+}
+
+int64_t tiles_per_head(const h3_shape* s) { return (s->seq_buf + kTileKeys - 1) / kTileKeys; }
+
+// Workspace layout: for batch b, the K images of all heads, then the V images:
+//   [b][K|V][head][tile] x 16 KiB.
+size_t batch_ws_bytes(const h3_shape* s) {
+  return 2 * (size_t)s->num_heads * (size_t)tiles_per_head(s) * (size_t)kTileBytes;
+}
+size_t workspace_bytes(const h3_shape* s) { return (size_t)s->batch * batch_ws_bytes(s); }
+
+h3_status launched() { return hipGetLastError() == hipSuccess ? H3_OK : H3_ERR_LAUNCH; }
+
+#define H3_TRY(expr)                   \
+  do {                                 \
+    const h3_status st_ = (expr);      \
+    if (st_ != H3_OK) return st_;      \
+  } while (0)
+
+h3_status check_workspace(const h3_shape* s, const void* ws, size_t bytes) {
+  const size_t need = workspace_bytes(s);
+  if (need > 0 && (!ws || bytes < need)) return H3_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return H3_ERR_ALIGN;
+  return H3_OK;
+}
+
+h3_status check_norm(const void* w, int64_t w_head_stride, float eps, const h3_rope* rope,
+                     int64_t max_valid, RopeArgs* ra) {
+  H3_TRY(check_weights(w, w, w_head_stride));
+  H3_TRY(check_rope(rope, max_valid, ra));
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return H3_ERR_SHAPE;
+  return H3_OK;
+}
+
+// ---------------------------------------------------------------- stage 1: K/V pack
+h3_status do_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
+                     float eps, const h3_rope* rope, const h3_shape* shp, void* workspace,
+                     size_t ws_bytes, hipStream_t stream) {
+  int64_t max_valid = 0;
+  H3_TRY(check_shape(shp, &max_valid));
+  if (!k || !v) return H3_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v)) return H3_ERR_ALIGN;
+  const bool norm = w_k != nullptr;
+  RopeArgs ra{};
+  if (norm) H3_TRY(check_norm(w_k, w_head_stride, eps, rope, max_valid, &ra));
+  H3_TRY(check_workspace(shp, workspace, ws_bytes));
+  H3_TRY(check_device());
+  const int64_t S = shp->seq_buf, tph = tiles_per_head(shp);
+  const size_t per_batch = batch_ws_bytes(shp);
+  for (int b = 0; b < shp->batch; ++b) {
+    const int64_t n = shp->seq_valid[b];
+    if (n == 0) continue;
+    char* ws = static_cast<char*>(workspace) + b * per_batch;
+    PackArgs pa{};
+    pa.k = static_cast<const __bf16*>(k) + b * S * shp->in_row_stride;
+    pa.v = static_cast<const __bf16*>(v) + b * S * shp->in_row_stride;
+    pa.w_k = static_cast<const __bf16*>(w_k);
+    pa.w_head_stride = w_head_stride;
+    pa.in_stride = shp->in_row_stride;
+    pa.n_valid = n;
+    pa.tiles_per_head = tph;
+    pa.eps = eps;
+    pa.rope = ra;
+    pa.k_img = ws;
+    pa.v_img = ws + per_batch / 2;
+    const dim3 grid((unsigned)((n + kTileKeys - 1) / kTileKeys), (unsigned)shp->num_heads);
+    if (norm)
+      kv_pack_kernel<true><<<grid, 128, 0, stream>>>(pa);
+    else
+      kv_pack_kernel<false><<<grid, 128, 0, stream>>>(pa);
+    H3_TRY(launched());
+  }
+  return H3_OK;
+}
+
+// ---------------------------------------------------------------- stage 2: attention
+h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head_stride,
+                         float eps, const h3_rope* rope, float softmax_scale,
+                         const h3_shape* shp, const void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  int64_t max_valid = 0;
+  H3_TRY(check_shape(shp, &max_valid));
+  if (!q || !o) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  const bool norm = w_q != nullptr;
+  RopeArgs ra{};
+  if (norm) H3_TRY(check_norm(w_q, w_head_stride, eps, rope, max_valid, &ra));
+  H3_TRY(check_workspace(shp, workspace, ws_bytes));
+  H3_TRY(check_device());
+  const int H = shp->num_heads;
+  const int64_t S = shp->seq_buf;
+  if (S == 0) return H3_OK;
+  const int m_tiles = (int)((S + kBM - 1) / kBM);
+  const size_t per_batch = batch_ws_bytes(shp);
+  for (int b = 0; b < shp->batch; ++b) {
+    const char* ws = static_cast<const char*>(workspace) + b * per_batch;
+    AttnArgs aa{};
+    aa.q = static_cast<const __bf16*>(q) + b * S * shp->in_row_stride;
+    aa.o = static_cast<__bf16*>(o) + b * S * shp->out_row_stride;
+    aa.k_img = ws;
+    aa.v_img = ws + per_batch / 2;
+    aa.tiles_per_head = tiles_per_head(shp);
+    aa.in_stride = shp->in_row_stride;
+    aa.out_stride = shp->out_row_stride;
+    aa.n_valid = shp->seq_valid[b];
+    aa.seq_buf = S;
+    aa.heads = H;
+    aa.m_tiles = m_tiles;
+    aa.scale_log2 = softmax_scale * 1.4426950408889634f;
+    aa.w_q = static_cast<const __bf16*>(w_q);
+    aa.w_head_stride = w_head_stride;
+    aa.eps = eps;
+    aa.rope = ra;
+    const unsigned blocks = (unsigned)((int64_t)H * m_tiles);
+    if (norm)
+      attn_fwd_kernel<kRB, true><<<blocks, 256, 0, stream>>>(aa);
+    else
+      attn_fwd_kernel<kRB, false><<<blocks, 256, 0, stream>>>(aa);
+    H3_TRY(launched());
+  }
+  return H3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* h3_status_string(h3_status s) {
+  switch (s) {
+    case H3_OK: return "H3_OK";
+    case H3_ERR_NULL: return "H3_ERR_NULL: a required pointer is NULL";
+    case H3_ERR_SHAPE: return "H3_ERR_SHAPE: inconsistent sizes or arguments";
+    case H3_ERR_ALIGN: return "H3_ERR_ALIGN: pointer or stride not 16-byte aligned";
+    case H3_ERR_UNSUPPORTED: return "H3_ERR_UNSUPPORTED: head_dim or RoPE layout not supported";
+    case H3_ERR_DEVICE: return "H3_ERR_DEVICE: no current gfx950 device";
+    case H3_ERR_LAUNCH: return "H3_ERR_LAUNCH: kernel launch failed";
+    case H3_ERR_WORKSPACE: return "H3_ERR_WORKSPACE: workspace missing or too small";
+  }
+  return "unknown h3_status";
+}
+
+int h3_version(void) { return 100; }
+
+h3_status h3_qk_rmsnorm_rope(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                             const void* w_q, const void* w_k, int64_t w_head_stride,
+                             float eps, const h3_rope* rope, const h3_shape* shape,
+                             hipStream_t stream) {
+  int64_t max_valid = 0;
+  H3_TRY(check_shape(shape, &max_valid));
+  if (!q_in || !k_in || !q_out || !k_out) return H3_ERR_NULL;
+  if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q_out) || !aligned16(k_out))
+    return H3_ERR_ALIGN;
+  H3_TRY(check_weights(w_q, w_k, w_head_stride));
+  RopeArgs ra{};
+  H3_TRY(check_rope(rope, max_valid, &ra));
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return H3_ERR_SHAPE;
+  if ((q_out == q_in || k_out == k_in) && shape->in_row_stride != shape->out_row_stride)
+    return H3_ERR_SHAPE;
+  H3_TRY(check_device());
+  const int64_t S = shape->seq_buf;
+  for (int b = 0; b < shape->batch; ++b) {
+    const int64_t n = shape->seq_valid[b];
+    if (n == 0) continue;
+    PrologueArgs pa{};
+    pa.q_in = static_cast<const __bf16*>(q_in) + b * S * shape->in_row_stride;
+    pa.k_in = static_cast<const __bf16*>(k_in) + b * S * shape->in_row_stride;
+    pa.q_out = static_cast<__bf16*>(q_out) + b * S * shape->out_row_stride;
+    pa.k_out = static_cast<__bf16*>(k_out) + b * S * shape->out_row_stride;
+    pa.w_q = static_cast<const __bf16*>(w_q);
+    pa.w_k = static_cast<const __bf16*>(w_k);
+    pa.w_head_stride = w_head_stride;
+    pa.in_stride = shape->in_row_stride;
+    pa.out_stride = shape->out_row_stride;
+    pa.n_valid = n;
+    pa.heads = shape->num_heads;
+    pa.eps = eps;
+    pa.rope = ra;
+    qk_norm_rope_kernel<<<(unsigned)n, 256, 0, stream>>>(pa);
+    H3_TRY(launched());
+  }
+  return H3_OK;
+}
+
+size_t h3_attn_workspace_size(const h3_shape* shape) {
+  int64_t max_valid = 0;
+  if (check_shape(shape, &max_valid) != H3_OK) return 0;
+  return workspace_bytes(shape);
+}
+
+h3_status h3_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
+                     float eps, const h3_rope* rope, const h3_shape* shape, void* workspace,
+                     size_t workspace_bytes_, hipStream_t stream) {
+  return do_kv_pack(k, v, w_k, w_head_stride, eps, rope, shape, workspace, workspace_bytes_,
+                    stream);
+}
+
+h3_status h3_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head_stride,
+                         float eps, const h3_rope* rope, float softmax_scale,
+                         const h3_shape* shape, const void* workspace, size_t workspace_bytes_,
+                         hipStream_t stream) {
+  return do_attn_packed(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape, workspace,
+                        workspace_bytes_, stream);
+}
+
+h3_status h3_attn_varlen(const void* q, const void* k, const void* v, void* o,
+                         float softmax_scale, const h3_shape* shape, void* workspace,
+                         size_t workspace_bytes_, hipStream_t stream) {
+  // validate everything the second stage needs before launching the first
+  if (!q || !o) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  H3_TRY(do_kv_pack(k, v, nullptr, 0, 0.0f, nullptr, shape, workspace, workspace_bytes_,
+                    stream));
+  return do_attn_packed(q, o, nullptr, 0, 0.0f, nullptr, softmax_scale, shape, workspace,
+                        workspace_bytes_, stream);
+}
+
+h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
+                        const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
+                        const h3_rope* rope, float softmax_scale, const h3_shape* shape,
+                        void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+  if (!q || !o || !w_q || !w_k) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  H3_TRY(check_weights(w_q, w_k, w_head_stride));
+  H3_TRY(do_kv_pack(k, v, w_k, w_head_stride, eps, rope, shape, workspace, workspace_bytes_,
+                    stream));
+  return do_attn_packed(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape, workspace,
+                        workspace_bytes_, stream);
+}
+
+}  // extern "C"

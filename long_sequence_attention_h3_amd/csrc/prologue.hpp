@@ -1,0 +1,307 @@
+// prologue.hpp — per-head RMSNorm + rotary embedding for Q and K, and the K/V
+// repacking pre-pass of the attention kernel.
+//
+// Pages: "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH3 的实时服务"
+// (Chinese translation of the vLLM blog post), §3.2 (Q/K RMSNorm and RoPE fused into
+// one operator) and §3.1 (RoPE rows are built per token; the packed sequence keeps
+// only its valid tokens).
+//
+// Every kernel that normalises and rotates a head row goes through the helpers in
+// this file with the same operation order, so the standalone prologue, the K pre-pass
+// and the Q prologue fused into attention produce bit-identical bf16 values.
+#pragma once
+
+#include "common.hpp"
+
+namespace h3 {
+
+// ---------------------------------------------------------------------------------
+// Rotary geometry.
+//
+// 1-D tokens: pair (j, j + 64), j = 0..63, frequency theta^(-2j/128), position = token.
+// 3-axis tokens: channel sections (s0, s1, s2) at offsets (0, s0, s0 + s1); inside a
+// section of size s, pair (off + j, off + j + s/2), frequency theta^(-2j/s), position
+// pt / ph / pw.  With sections that are multiples of 16 every 8-channel chunk lies in
+// one section and one half of it, so a chunk's rotation partner is a whole chunk.
+// Pairs are numbered 0..63 globally: 1-D pair j is j; 3-axis pair j of the section at
+// offset off is off/2 + j.
+
+// Frequencies divided by 2*pi ("revolutions per position unit") for the 64 pairs of
+// each mode, computed in fp64 once per workgroup into LDS.
+struct FreqTable {
+  double one_d[64];
+  double three[64];
+};
+
+__device__ __forceinline__ void fill_freq_table(FreqTable* t, const RopeArgs& r, int tid,
+                                                int nthreads) {
+  const double inv_2pi = 0.15915494309189533577;  // 1 / (2 pi)
+  for (int i = tid; i < 128; i += nthreads) {
+    const int p = i & 63;
+    if (i < 64) {
+      t->one_d[p] = pow(r.theta, -2.0 * (double)p / 128.0) * inv_2pi;
+    } else {
+      int off = 0, s = r.sec[0];
+      if (2 * p >= r.sec[0] + r.sec[1]) {
+        off = r.sec[0] + r.sec[1];
+        s = r.sec[2];
+      } else if (2 * p >= r.sec[0]) {
+        off = r.sec[0];
+        s = r.sec[1];
+      }
+      const int j = p - off / 2;
+      t->three[p] = (s > 0) ? pow(r.theta, -2.0 * (double)j / (double)s) * inv_2pi : 0.0;
+    }
+  }
+}
+
+// Where one 8-channel chunk of a token's row sits in the rotation.
+struct ChunkRot {
+  int partner;      // chunk holding the other member of each pair
+  int pair0;        // global pair index of the chunk's first channel
+  bool first;       // chunk holds the first members (y_j) rather than y_{j+s/2}
+  bool three_axis;  // 3-axis table and position
+  double pos;       // position along the chunk's axis
+};
+
+__device__ __forceinline__ ChunkRot chunk_rotation(const RopeArgs& r, int64_t token, int cc) {
+  ChunkRot c;
+  if (token < r.n_1d) {
+    c.three_axis = false;
+    c.first = cc < 8;
+    c.partner = cc ^ 8;
+    c.pair0 = (cc & 7) * 8;
+    c.pos = (double)token;
+    return c;
+  }
+  c.three_axis = true;
+  const int64_t k = token - r.n_1d;
+  const int64_t hw = (int64_t)r.gh * r.gw;
+  const int64_t pt = k / hw, ph = (k / r.gw) % r.gh, pw = k % r.gw;
+  const int ch = cc * 8;
+  int off, s;
+  int64_t pos;
+  if (ch < r.sec[0]) {
+    off = 0; s = r.sec[0]; pos = pt;
+  } else if (ch < r.sec[0] + r.sec[1]) {
+    off = r.sec[0]; s = r.sec[1]; pos = ph;
+  } else {
+    off = r.sec[0] + r.sec[1]; s = r.sec[2]; pos = pw;
+  }
+  const int half = s / 2, u = ch - off;
+  c.first = u < half;
+  c.partner = c.first ? cc + half / 8 : cc - half / 8;
+  c.pair0 = off / 2 + (c.first ? u : u - half);
+  c.pos = (double)pos;
+  return c;
+}
+
+// cos and sin of 2*pi*frac(pos * f): the product and its reduction to one revolution in
+// fp64 (positions reach ~1e5, where an fp32 angle would be off by ~1e-2 rad), the
+// trigonometry on the reduced fp32 argument.
+__device__ __forceinline__ void rope_cos_sin(double pos, double f, float* c, float* s) {
+  const double rev = pos * f;
+  const float fr = (float)(rev - rint(rev));
+  *c = __builtin_amdgcn_cosf(fr);  // cos(2*pi*fr)
+  *s = __builtin_amdgcn_sinf(fr);  // sin(2*pi*fr)
+}
+
+// Sum of squares of one chunk (8 values), accumulated in index order.
+__device__ __forceinline__ float chunk_sumsq(const float* x) {
+  float p = x[0] * x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) p = fmaf(x[e], x[e], p);
+  return p;
+}
+
+// The row's inverse RMS from its sum of squares.  The sum over the 16 chunk partials
+// is always formed as the pairwise tree ((p0+p1)+(p2+p3)) + ... , i.e. partials of
+// chunks c and c^1 first, then c^2, c^4, c^8; callers reproduce that tree exactly.
+__device__ __forceinline__ float inv_rms(float sumsq, float eps) {
+  return __builtin_amdgcn_rsqf(sumsq * (1.0f / kHeadDim) + eps);
+}
+
+// Normalise and rotate one chunk.  x / xp: own and partner chunk values; w / wp: their
+// weights; returns the 8 rotated values.
+__device__ __forceinline__ void norm_rotate_chunk(const float* x, const float* xp,
+                                                  const float* w, const float* wp,
+                                                  float inv, const ChunkRot& cr,
+                                                  const FreqTable* ft, float* out) {
+  const double* tab = cr.three_axis ? ft->three : ft->one_d;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = (x[e] * inv) * w[e];
+    const float yp = (xp[e] * inv) * wp[e];
+    float c, s;
+    rope_cos_sin(cr.pos, tab[cr.pair0 + e], &c, &s);
+    // first member:  y_j cos - y_{j+s/2} sin;  second member:  y_{j+s/2} cos + y_j sin
+    out[e] = cr.first ? fmaf(y, c, -(yp * s)) : fmaf(y, c, yp * s);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// One (token, head) row handled by 16 consecutive lanes, lane `cc` owning chunk cc.
+// Loads, normalises, rotates and returns the lane's 8 output values.  `row` points at
+// the head's 128 inputs, `w` at the head's 128 weights.  All 16 lanes must be active.
+__device__ __forceinline__ void norm_rotate_row16(const __bf16* row, const __bf16* w,
+                                                  float eps, const ChunkRot& cr, int cc,
+                                                  const FreqTable* ft, float* out) {
+  const u32x4 raw = *reinterpret_cast<const u32x4*>(row + cc * 8);
+  float x[8];
+  unpack8(raw, x);
+  float ss = chunk_sumsq(x);
+  ss += __shfl_xor(ss, 1, 16);
+  ss += __shfl_xor(ss, 2, 16);
+  ss += __shfl_xor(ss, 4, 16);
+  ss += __shfl_xor(ss, 8, 16);
+  const float inv = inv_rms(ss, eps);
+  // partner chunk's values from the lane that owns it
+  const int base = (threadIdx.x & 63) & ~15;
+  u32x4 praw;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) praw[i] = __shfl(raw[i], base + cr.partner, 64);
+  float xp[8], wv[8], wpv[8];
+  unpack8(praw, xp);
+  unpack8(*reinterpret_cast<const u32x4*>(w + cc * 8), wv);
+  unpack8(*reinterpret_cast<const u32x4*>(w + cr.partner * 8), wpv);
+  norm_rotate_chunk(x, xp, wv, wpv, inv, cr, ft, out);
+}
+
+struct PrologueArgs {
+  const __bf16* q_in;
+  const __bf16* k_in;
+  __bf16* q_out;
+  __bf16* k_out;
+  const __bf16* w_q;
+  const __bf16* w_k;
+  int64_t w_head_stride;  // elements; 0 = shared
+  int64_t in_stride, out_stride;  // row strides, elements
+  int64_t n_valid;
+  int heads;
+  float eps;
+  RopeArgs rope;
+};
+
+// Standalone fused Q/K RMSNorm + RoPE.  One workgroup per token: the rotation of a
+// token is the same for every head, so it is set up once and reused for 2*H rows.
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
+  const int64_t t = blockIdx.x;
+  if (t >= a.n_valid) return;
+  __shared__ FreqTable ft;
+  fill_freq_table(&ft, a.rope, threadIdx.x, blockDim.x);
+  __syncthreads();
+  const int cc = threadIdx.x & 15;
+  const ChunkRot cr = chunk_rotation(a.rope, t, cc);
+  for (int r = threadIdx.x >> 4; r < 2 * a.heads; r += blockDim.x >> 4) {
+    const bool is_q = r < a.heads;
+    const int h = is_q ? r : r - a.heads;
+    const __bf16* in = (is_q ? a.q_in : a.k_in) + t * a.in_stride + (int64_t)h * kHeadDim;
+    const __bf16* w = (is_q ? a.w_q : a.w_k) + (int64_t)h * a.w_head_stride;
+    float y[8];
+    norm_rotate_row16(in, w, a.eps, cr, cc, &ft, y);
+    __bf16* out = (is_q ? a.q_out : a.k_out) + t * a.out_stride + (int64_t)h * kHeadDim;
+    // every lane has read its partner chunk before any lane of the row stores (the
+    // shuffles above are complete), so in-place operation is safe
+    *reinterpret_cast<u32x4*>(out + cc * 8) = pack8(y);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// K/V pre-pass of the attention kernel.
+//
+// For head h, key tile kt (keys 64*kt .. 64*kt+63) it writes two 16 KiB images that the
+// attention kernel copies linearly into LDS:
+//   K image: row r (key), chunk c (channels 8c..8c+7) at 16-byte slot
+//            r*16 + (c ^ swap23(r & 15)),
+//   V image: channel d, key chunk c (keys 8c..8c+7 of channel d) at slot
+//            d*8 + (c ^ vswz(d)),   vswz(d) = (d & 7) ^ ((d >> 3) & 1),
+// swap23 exchanging bits 2 and 3.  The XOR swizzles make the attention kernel's LDS
+// reads conflict-free whether the LDS serves 8 or 16 lanes of a 16-byte read per
+// cycle.  Keys >= N are written as zeros.  With `norm` set, K rows are
+// RMS-normalised and rotated on the way (the layer path); otherwise copied.
+struct PackArgs {
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* w_k;
+  int64_t w_head_stride;
+  int64_t in_stride;
+  int64_t n_valid;
+  int64_t tiles_per_head;  // capacity of the image arrays per head
+  float eps;
+  RopeArgs rope;
+  char* k_img;
+  char* v_img;
+};
+
+__device__ __forceinline__ int swap23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+__device__ __forceinline__ int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
+
+template <bool kNorm>
+__global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
+  const int64_t kt = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  __shared__ FreqTable ft;
+  if (kNorm) {
+    fill_freq_table(&ft, a.rope, tid, blockDim.x);
+    __syncthreads();
+  }
+  const int64_t key0 = kt * kTileKeys;
+  char* kimg = a.k_img + ((int64_t)h * a.tiles_per_head + kt) * kTileBytes;
+  char* vimg = a.v_img + ((int64_t)h * a.tiles_per_head + kt) * kTileBytes;
+  const int64_t hoff = (int64_t)h * kHeadDim;
+
+  // K: 64 rows x 16 chunks; 8 rows per pass (16 lanes per row).
+  const int cc = tid & 15;
+  for (int r = tid >> 4; r < kTileKeys; r += 8) {
+    const int64_t key = key0 + r;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    // the whole 16-lane row group takes the same branch (one key per group)
+    if (key < a.n_valid) {
+      const __bf16* row = a.k + key * a.in_stride + hoff;
+      if (kNorm) {
+        const ChunkRot cr = chunk_rotation(a.rope, key, cc);
+        float y[8];
+        norm_rotate_row16(row, a.w_k + (int64_t)h * a.w_head_stride, a.eps, cr, cc, &ft, y);
+        out = pack8(y);
+      } else {
+        out = *reinterpret_cast<const u32x4*>(row + cc * 8);
+      }
+    }
+    *reinterpret_cast<u32x4*>(kimg + (r * 16 + (cc ^ swap23(r & 15))) * 16) = out;
+  }
+
+  // V: thread (key chunk kc, channel chunk cg) transposes an 8 x 8 block:
+  // reads keys 8kc..8kc+7 at channels 8cg..8cg+7, writes 8 image chunks (one per
+  // channel, 8 keys each).
+  {
+    const int kc = tid & 7, cg = tid >> 3;  // 8 x 16 = 128 threads
+    uint32_t x[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t key = key0 + kc * 8 + e;
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (key < a.n_valid)
+        raw = *reinterpret_cast<const u32x4*>(a.v + key * a.in_stride + hoff + cg * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[e][i] = raw[i];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {  // channel 8cg + c
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // keys 2i and 2i+1 of channel c: 16-bit halves (c & 1) of dword c/2
+        const uint32_t lo = x[2 * i][c >> 1], hi = x[2 * i + 1][c >> 1];
+        o[i] = (c & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                       : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
+      const int d = cg * 8 + c;
+      *reinterpret_cast<u32x4*>(vimg + (d * 8 + (kc ^ vswz(d))) * 16) = o;
+    }
+  }
+}
+
+}  // namespace h3

@@ -68,19 +68,16 @@ def tail_fill_bits(mode: str) -> int | None:
 
 
 def generate(w: Workload, tail: str | None = "nan", seed: int | None = None,
-             shape_override: dict | None = None) -> dict:
+             n_valid: list | None = None) -> dict:
     """Seeded bf16 inputs on the CPU.
 
     Draw order from one ``torch.Generator`` seeded with ``seed`` (default
     ``w.seed``): Q, K, V as fp32 N(0,1) of shape [B, S, H, D] cast to bf16
     (round-to-nearest-even), then w_q = 1 + 0.1 * N(0,1) [D], then w_k likewise.
-    Rows [N, S) of Q, K and V are then overwritten with ``tail``.
+    Rows [N_b, S) of Q, K and V are then overwritten with ``tail``; ``n_valid`` gives
+    N_b per batch (default: ``w.n_valid`` for every batch).
     """
     B, S, H, D = w.batch, w.seq_buf, w.heads, w.head_dim
-    if shape_override:
-        B = shape_override.get("batch", B)
-        S = shape_override.get("seq_buf", S)
-        H = shape_override.get("heads", H)
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed if seed is None else seed)
     out = {}
@@ -91,7 +88,8 @@ def generate(w: Workload, tail: str | None = "nan", seed: int | None = None,
         out[name] = (1.0 + 0.1 * torch.randn((D,), generator=g, dtype=torch.float32)).to(
             torch.bfloat16)
     fill = tail_fill_bits(tail)
-    n_valid = [w.n_valid] * B
+    n_valid = [w.n_valid] * B if n_valid is None else list(n_valid)
+    assert len(n_valid) == B and all(0 <= n <= S for n in n_valid)
     if fill is not None:
         for name in ("q", "k", "v"):
             bits = out[name].view(torch.int16)

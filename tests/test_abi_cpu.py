@@ -1,0 +1,151 @@
+"""The C ABI on the host: the library loads, exports every declared entry point, and
+rejects bad arguments before touching a device (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from long_sequence_attention_h3_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3attn.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+WS = 0x20000    # 256-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = B.lib()
+    for code, name in B.STATUS_NAMES.items():
+        assert L.h3_status_string(code).decode().startswith(name)
+    assert L.h3_status_string(99) == b"unknown h3_status"
+    assert L.h3_version() >= 100
+
+
+def shape(B_=1, H=2, D=128, S=1024, valid=(1000,), sin=None, sout=None):
+    arr = (ctypes.c_int64 * len(valid))(*valid)
+    s = B.Shape(B_, H, D, S, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)),
+                H * D if sin is None else sin, H * D if sout is None else sout)
+    s._keep = arr
+    return s
+
+
+def rope(n_1d=1000, sections=(0, 0, 0), grid=(0, 0, 0), theta=1e4):
+    return B.make_rope(theta, n_1d, sections, grid)
+
+
+def varlen(s, q=FAKE, ws=WS, ws_bytes=None, scale=0.088):
+    L = B.lib()
+    need = L.h3_attn_workspace_size(ctypes.byref(s)) if ws_bytes is None else ws_bytes
+    return L.h3_attn_varlen(q, FAKE, FAKE, FAKE, scale, ctypes.byref(s), ws, need, None)
+
+
+def layer(s, r, w=FAKE, whs=0, eps=1e-6):
+    L = B.lib()
+    need = L.h3_attn_workspace_size(ctypes.byref(s))
+    return L.h3_attn_layer(FAKE, FAKE, FAKE, FAKE, w, w, whs, eps, ctypes.byref(r), 0.088,
+                           ctypes.byref(s), WS, need, None)
+
+
+def prologue(s, r, q_out=FAKE, eps=1e-6):
+    return B.lib().h3_qk_rmsnorm_rope(FAKE, FAKE, q_out, FAKE, FAKE, FAKE, 0, eps,
+                                      ctypes.byref(r), ctypes.byref(s), None)
+
+
+def test_workspace_size_formula():
+    L = B.lib()
+    assert L.h3_attn_workspace_size(ctypes.byref(shape(H=42, S=58816, valid=(58758,)))) == \
+        2 * 42 * 919 * 16384
+    assert L.h3_attn_workspace_size(ctypes.byref(shape(S=65, valid=(1,)))) == 2 * 2 * 2 * 16384
+    assert L.h3_attn_workspace_size(ctypes.byref(shape(B_=3, S=64, valid=(1, 2, 3)))) == \
+        3 * 2 * 2 * 1 * 16384
+    assert L.h3_attn_workspace_size(ctypes.byref(shape(D=64))) == 0
+    assert L.h3_attn_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(D=64), 4),                      # head_dim must be 128
+    (dict(valid=(1025,)), 2),             # N > S
+    (dict(valid=(-1,)), 2),               # N < 0
+    (dict(sin=255), 2),                   # stride < H*D
+    (dict(sin=260), 3),                   # stride not a multiple of 8 elements
+    (dict(H=0), 2),
+    (dict(B_=2, valid=(10, 2000)), 2),    # second batch N > S
+])
+def test_shape_validation(kwargs, code):
+    assert varlen(shape(**kwargs)) == code
+
+
+def test_pointer_and_workspace_validation():
+    s = shape()
+    assert varlen(s, q=0) == 1                       # NULL input
+    assert varlen(s, q=FAKE + 2) == 3                # misaligned input
+    assert varlen(s, ws=0) == 7                      # workspace missing
+    assert varlen(s, ws_bytes=1000) == 7             # workspace too small
+    assert varlen(s, ws=WS + 16) == 3                # workspace not 256-byte aligned
+    assert varlen(s, scale=0.0) == 2                 # softmax scale must be > 0
+    assert varlen(s, scale=float("nan")) == 2
+    assert B.lib().h3_attn_varlen(FAKE, FAKE, FAKE, FAKE, 0.1, None, WS, 1, None) == 1
+
+
+def test_rope_and_weight_validation():
+    s = shape(valid=(1000,))
+    assert layer(s, rope(n_1d=100)) == 4                        # 3-axis tokens, no sections
+    assert layer(s, rope(n_1d=100, sections=(32, 48, 40), grid=(10, 10, 10))) == 4
+    assert layer(s, rope(n_1d=100, sections=(40, 40, 48), grid=(10, 10, 10))) == 4  # not /16
+    assert layer(s, rope(n_1d=100, sections=(32, 48, 48), grid=(8, 10, 10))) == 4   # grid small
+    assert layer(s, rope(theta=0.0)) == 4
+    assert layer(s, rope(), w=0) == 1
+    assert layer(s, rope(), whs=64) == 2                       # per-head stride < D
+    assert layer(s, rope(), eps=-1.0) == 2
+    assert prologue(s, rope(), q_out=0) == 1
+    # in place needs equal input and output strides
+    s2 = shape(sin=512, sout=256)
+    assert B.lib().h3_qk_rmsnorm_rope(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1e-6,
+                                      ctypes.byref(rope()), ctypes.byref(s2), None) == 2
+
+
+def test_stage_entry_points_validate():
+    L = B.lib()
+    s = shape()
+    need = L.h3_attn_workspace_size(ctypes.byref(s))
+    r = rope()
+    assert L.h3_kv_pack(0, FAKE, None, 0, 0.0, None, ctypes.byref(s), WS, need, None) == 1
+    assert L.h3_kv_pack(FAKE, FAKE, None, 0, 0.0, None, ctypes.byref(s), WS, need - 1, None) == 7
+    assert L.h3_kv_pack(FAKE, FAKE, FAKE, 0, 1e-6, None, ctypes.byref(s), WS, need, None) == 1
+    assert L.h3_attn_packed(FAKE, 0, None, 0, 0.0, None, 0.1, ctypes.byref(s), WS, need,
+                            None) == 1
+    assert L.h3_attn_packed(FAKE, FAKE, FAKE, 0, 1e-6, ctypes.byref(rope(n_1d=10)), 0.1,
+                            ctypes.byref(s), WS, need, None) == 4
+    assert L.h3_attn_packed(FAKE, FAKE, None, 0, 0.0, None, -1.0, ctypes.byref(s), WS, need,
+                            None) == 2
+    del r
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
+def test_valid_call_without_device_fails_loudly():
+    L = B.lib()
+    s = shape()
+    assert varlen(s) == 5
+    assert layer(s, rope()) == 5
+    assert prologue(s, rope()) == 5
+    need = L.h3_attn_workspace_size(ctypes.byref(s))
+    assert L.h3_kv_pack(FAKE, FAKE, None, 0, 0.0, None, ctypes.byref(s), WS, need, None) == 5
+    assert L.h3_attn_packed(FAKE, FAKE, None, 0, 0.0, None, 0.1, ctypes.byref(s), WS, need,
+                            None) == 5

@@ -1,0 +1,125 @@
+"""Edge cases of the C ABI on the GPU, each against the fp64 oracle or an exact property:
+empty and one-token sequences, a valid length equal to the buffer, one key in the last
+tile, many all-tail tiles, two batches of different lengths, a fused QKV buffer (row
+stride 3*H*D), per-head norm weights, and the all-equal-keys property at full length."""
+import numpy as np
+import pytest
+import torch
+
+from long_sequence_attention_h3_amd import binding as B
+from long_sequence_attention_h3_amd import workloads as W
+
+from parity_helpers import (assert_close, assert_tail_zero, gpu_layer, gpu_rope, gpu_varlen,
+                            oracle_layer, oracle_varlen, rows_of, say, scale_of, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    return torch.device("cuda:0")
+
+
+def small(n, s, heads=3, seed=50, batch=1, **kw):
+    return W.Workload(f"edge_{n}of{s}", heads=heads, n_valid=n, seq_buf=s, seed=seed,
+                      batch=batch, **kw)
+
+
+@pytest.mark.parametrize("n,s", [(1, 1), (1, 64), (64, 64), (65, 128), (127, 128),
+                                 (300, 2000), (2048, 2048), (777, 1000)])
+def test_ragged_lengths_match_oracle(n, s, dev):
+    w = small(n, s)
+    inp = W.generate(w, tail="nan")
+    say(f"[edge] N={n} S={s}")
+    for entry, run, orc in (("layer", gpu_layer, oracle_layer),
+                            ("varlen", gpu_varlen, oracle_varlen)):
+        out = run(w, to_dev(inp, dev))
+        assert_tail_zero(out, inp["n_valid"], entry)
+        rows = list(range(n))
+        assert_close(rows_of(out, rows), orc(w, inp, rows), f"{entry} N={n} S={s}")
+
+
+def test_single_token_returns_its_value_exactly(dev):
+    w = small(1, 80, heads=4, seed=51)
+    inp = W.generate(w, tail="nan")
+    out = gpu_varlen(w, to_dev(inp, dev))
+    assert torch.equal(out[0, 0].cpu().view(torch.int16), inp["v"][0, 0].view(torch.int16))
+    assert_tail_zero(out, [1], "N=1")
+
+
+@pytest.mark.parametrize("entry", ["layer", "varlen"])
+def test_empty_sequence_gives_zeros(entry, dev):
+    w = small(0, 200, seed=52)
+    inp = W.generate(w, tail="nan")
+    run = gpu_layer if entry == "layer" else gpu_varlen
+    out = run(w, to_dev(inp, dev), out=torch.full((1, 200, 3, 128), float("nan"),
+                                                 dtype=torch.bfloat16, device=dev))
+    assert_tail_zero(out, [0], f"{entry} N=0")
+
+
+def test_two_batches_of_different_lengths(dev):
+    w = small(700, 1024, heads=2, seed=53, batch=2)
+    inp = W.generate(w, tail="nan", n_valid=[700, 1024])
+    d = to_dev(inp, dev)
+    say("[edge] batch 2, N = 700 and 1024")
+    for entry, run, orc in (("layer", gpu_layer, oracle_layer),
+                            ("varlen", gpu_varlen, oracle_varlen)):
+        out = run(w, d)
+        assert_tail_zero(out, inp["n_valid"], entry)
+        for b, n in enumerate(inp["n_valid"]):
+            rows = list(range(n))
+            ref = orc(w, inp, rows, batch=b) if entry == "varlen" else \
+                oracle_layer(w, inp, rows, batch=b)
+            assert_close(rows_of(out, rows, batch=b), ref, f"{entry} batch {b}")
+
+
+def test_fused_qkv_buffer_row_stride(dev):
+    """Q, K and V as views of one [S, 3, H, D] buffer (row stride 3*H*D), output [S, H, D]."""
+    w = small(900, 1000, heads=4, seed=54)
+    inp = W.generate(w, tail="nan")
+    qkv = torch.stack([inp["q"][0], inp["k"][0], inp["v"][0]], dim=1).to(dev)  # [S,3,H,D]
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    assert q.stride(0) == 3 * 4 * 128
+    out = B.attn_layer(q, k, v, inp["w_q"].to(dev), inp["w_k"].to(dev), 900, w.eps,
+                       gpu_rope(w), scale_of(w))
+    torch.cuda.synchronize()
+    rows = list(range(900))
+    assert_close(rows_of(out.unsqueeze(0), rows), oracle_layer(w, inp, rows), "fused QKV")
+    ref = gpu_layer(w, to_dev(inp, dev))
+    assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16))
+
+
+def test_per_head_norm_weights(dev):
+    """w_head_stride = D: head h uses its own weights; checked against the oracle run
+    head by head with that head's weights."""
+    from oracle import oracle as O
+    w = small(500, 512, heads=3, seed=55)
+    inp = W.generate(w, tail="nan")
+    g = torch.Generator().manual_seed(56)
+    wq = (1 + 0.3 * torch.randn((3, 128), generator=g)).to(torch.bfloat16)
+    wk = (1 + 0.3 * torch.randn((3, 128), generator=g)).to(torch.bfloat16)
+    d = to_dev(inp, dev)
+    out = B.attn_layer(d["q"], d["k"], d["v"], wq.to(dev), wk.to(dev), 500, w.eps, gpu_rope(w),
+                       scale_of(w))
+    torch.cuda.synchronize()
+    rows = np.arange(500)
+    ref = O.attn_layer(W.bits(inp["q"][0]), W.bits(inp["k"][0]), W.bits(inp["v"][0]), 500,
+                       W.bits(wq), W.bits(wk), w.eps,
+                       O.make_rope(w.theta, 500), scale_of(w), rows, w_head_stride=128)
+    assert_close(rows_of(out, rows), ref, "per-head weights")
+
+
+def test_equal_keys_give_mean_of_values_at_full_length(dev):
+    """All valid K rows zero: every score is 0 after RMSNorm + RoPE, so each output row is
+    the mean of the valid V rows (any Q) - a property that holds at any size."""
+    w = W.WORKLOADS[2]
+    inp = W.generate(w, tail="nan")
+    inp["k"][0, : w.n_valid] = 0
+    d = to_dev(inp, dev)
+    say("[property] zero keys, full length")
+    out = gpu_layer(w, d)
+    mean = inp["v"][0, : w.n_valid].double().mean(0).numpy()            # [H, D]
+    rows = W.sample_rows(w, 256, 7)
+    got = rows_of(out, rows)
+    assert_close(got, np.broadcast_to(mean, got.shape), "mean of V")

@@ -1,0 +1,147 @@
+"""GPU parity of libh3attn against the fp64 oracle, on every workload size.
+
+Full row sets where the oracle finishes in seconds (the 2-head and 8-head workloads);
+at the full sequence length, sampled query rows (uniform without replacement, plus
+rows 0 and N-1 and every segment edge; the same rows for every head): 4,096 rows per
+head on the 6-head one-GPU share and 512 per head on the 42-head layers (4,096 per head
+there too when H3_FULL_SAMPLE=1).  Inputs are seeded bf16 N(0,1) with NaN-filled
+buffer tails.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from long_sequence_attention_h3_amd import binding as B
+from long_sequence_attention_h3_amd import workloads as W
+from oracle import oracle as O
+
+from parity_helpers import (assert_close, assert_tail_zero, gpu_layer, gpu_rope, gpu_varlen,
+                            oracle_layer, oracle_rope, oracle_varlen, rows_of, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+FULL = os.environ.get("H3_FULL_SAMPLE") == "1"
+ROWS_PER_HEAD = {0: None, 1: None, 2: 4096, 3: 4096 if FULL else 512, 4: 4096 if FULL else 512}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    return torch.device("cuda:0")
+
+
+_cache = {}
+
+
+def inputs(cfg):
+    if cfg not in _cache:
+        _cache.clear()
+        say(f"[inputs] workload {cfg} {W.WORKLOADS[cfg].name}")
+        _cache[cfg] = W.generate(W.WORKLOADS[cfg], tail="nan")
+    return _cache[cfg]
+
+
+def check_rows(cfg):
+    w = W.WORKLOADS[cfg]
+    per = ROWS_PER_HEAD[cfg]
+    rows = list(range(w.n_valid)) if per is None else W.sample_rows(w, per, 10_000 + cfg)
+    return rows
+
+
+CASES = [(cfg, entry) for cfg in (0, 1, 2, 3, 4) for entry in ("layer", "varlen")]
+
+
+@pytest.mark.parametrize("cfg,entry", CASES)
+def test_matches_oracle(cfg, entry, dev):
+    w = W.WORKLOADS[cfg]
+    inp = inputs(cfg)
+    say(f"[h3_attn_{entry}] workload {cfg} {w.name} H={w.heads} N={w.n_valid} S={w.seq_buf}")
+    run = gpu_layer if entry == "layer" else gpu_varlen
+    out = run(w, to_dev(inp, dev))
+    assert_tail_zero(out, inp["n_valid"], entry)
+    rows = check_rows(cfg)
+    ref = (oracle_layer if entry == "layer" else oracle_varlen)(w, inp, rows)
+    assert_close(rows_of(out, rows), ref, f"{entry} cfg{cfg}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 4])
+def test_prologue_matches_oracle(cfg, dev):
+    """bf16 outputs of h3_qk_rmsnorm_rope within bf16 rounding (2^-8 relative, plus the
+    fp32 trigonometry) of the fp64 RMSNorm + RoPE; buffer tail rows left untouched."""
+    w = W.WORKLOADS[cfg]
+    inp = inputs(cfg)
+    d = to_dev(inp, dev)
+    say(f"[h3_qk_rmsnorm_rope] workload {cfg} {w.name}")
+    sentinel = torch.full_like(d["q"], 7.0)
+    q_out, k_out = sentinel.clone(), sentinel.clone()
+    B.qk_rmsnorm_rope(d["q"], d["k"], d["w_q"], d["w_k"], inp["n_valid"], w.eps, gpu_rope(w),
+                      q_out=q_out, k_out=k_out)
+    torch.cuda.synchronize()
+    n = w.n_valid
+    assert torch.equal(q_out[0, n:], sentinel[0, n:]) and torch.equal(k_out[0, n:],
+                                                                      sentinel[0, n:])
+    toks = (np.arange(n) if n <= 8192 else
+            np.asarray(W.sample_rows(w, 2048, 20_000 + cfg)))
+    for name, x, wt, got in (("q", "q", "w_q", q_out), ("k", "k", "w_k", k_out)):
+        ref = O.prologue(W.bits(inp[x][0]), n, W.bits(inp[wt]), w.eps, oracle_rope(w), toks)
+        g = rows_of(got, toks)
+        err = np.abs(g - ref)
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-4
+        say(f"  prologue {name} cfg{cfg}: max|d|={err.max():.3e} worst ratio="
+            f"{(err / bound).max():.3f}")
+        assert np.all(err <= bound)
+
+
+def test_prologue_in_place(dev):
+    w = W.WORKLOADS[0]
+    inp = inputs(0)
+    d = to_dev(inp, dev)
+    q_ref, k_ref = B.qk_rmsnorm_rope(d["q"], d["k"], d["w_q"], d["w_k"], inp["n_valid"], w.eps,
+                                     gpu_rope(w))
+    q, k = d["q"].clone(), d["k"].clone()
+    B.qk_rmsnorm_rope(q, k, d["w_q"], d["w_k"], inp["n_valid"], w.eps, gpu_rope(w),
+                      q_out=q, k_out=k)
+    torch.cuda.synchronize()
+    n = w.n_valid
+    assert torch.equal(q[0, :n], q_ref[0, :n]) and torch.equal(k[0, :n], k_ref[0, :n])
+
+
+@pytest.mark.parametrize("cfg", [0, 4])
+def test_layer_equals_prologue_then_varlen_bitwise(cfg, dev):
+    """The fused layer and the two-call path round Q and K to bf16 identically."""
+    w = W.WORKLOADS[cfg]
+    inp = inputs(cfg)
+    d = to_dev(inp, dev)
+    say(f"[layer vs prologue+varlen] workload {cfg}")
+    fused = gpu_layer(w, d)
+    q2, k2 = B.qk_rmsnorm_rope(d["q"], d["k"], d["w_q"], d["w_k"], inp["n_valid"], w.eps,
+                               gpu_rope(w))
+    d2 = dict(d, q=q2, k=k2)
+    two = gpu_varlen(w, d2)
+    assert torch.equal(fused.view(torch.int16), two.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_tail_contents_never_matter(cfg, dev):
+    w = W.WORKLOADS[cfg]
+    outs = []
+    for tail in ("nan", "big", "zero"):
+        inp = W.generate(w, tail=tail)
+        say(f"[tail={tail}] workload {cfg}")
+        outs.append(gpu_layer(w, to_dev(inp, dev)).view(torch.int16))
+        outs.append(gpu_varlen(w, to_dev(inp, dev)).view(torch.int16))
+    for o in outs[2::2]:
+        assert torch.equal(o, outs[0])
+    for o in outs[3::2]:
+        assert torch.equal(o, outs[1])
+
+
+def test_deterministic_run_to_run(dev):
+    w = W.WORKLOADS[1]
+    d = to_dev(inputs(1), dev)
+    say("[determinism] workload 1")
+    a = gpu_layer(w, d).view(torch.int16).clone()
+    for _ in range(2):
+        assert torch.equal(gpu_layer(w, d).view(torch.int16), a)
