@@ -71,9 +71,10 @@ def oracle_layer(w: W.Workload, inp: dict, rows, batch: int = 0, n_valid=None):
                         scale_of(w), np.asarray(rows, dtype=np.int64))
 
 
-def oracle_varlen(w: W.Workload, inp: dict, rows, batch: int = 0):
+def oracle_varlen(w: W.Workload, inp: dict, rows, batch: int = 0, n_valid=None):
     return O.attn_varlen(W.bits(inp["q"][batch]), W.bits(inp["k"][batch]),
-                         W.bits(inp["v"][batch]), inp["n_valid"][batch], scale_of(w),
+                         W.bits(inp["v"][batch]),
+                         inp["n_valid"][batch] if n_valid is None else n_valid, scale_of(w),
                          np.asarray(rows, dtype=np.int64))
 
 

@@ -59,7 +59,7 @@ def test_empty_sequence_gives_zeros(entry, dev):
 
 
 def test_two_batches_of_different_lengths(dev):
-    w = small(700, 1024, heads=2, seed=53, batch=2)
+    w = small(700, 1024, heads=2, seed=53, batch=2, n_1d=1024)
     inp = W.generate(w, tail="nan", n_valid=[700, 1024])
     d = to_dev(inp, dev)
     say("[edge] batch 2, N = 700 and 1024")
@@ -69,8 +69,8 @@ def test_two_batches_of_different_lengths(dev):
         assert_tail_zero(out, inp["n_valid"], entry)
         for b, n in enumerate(inp["n_valid"]):
             rows = list(range(n))
-            ref = orc(w, inp, rows, batch=b) if entry == "varlen" else \
-                oracle_layer(w, inp, rows, batch=b)
+            ref = orc(w, inp, rows, batch=b, n_valid=n) if entry == "layer" else \
+                orc(w, inp, rows, batch=b)
             assert_close(rows_of(out, rows, batch=b), ref, f"{entry} batch {b}")
 
 
