@@ -13,10 +13,14 @@
 #include <cstring>
 
 #include "attention.hpp"
+#include "attention_pipelined.hpp"
 #include "prologue.hpp"
 
 #ifndef H3_ROWS_PER_WAVE_BLOCKS
-#define H3_ROWS_PER_WAVE_BLOCKS 1  // 32-row blocks of queries per wave
+#define H3_ROWS_PER_WAVE_BLOCKS 1  // 32-row blocks of queries per wave (simple kernel)
+#endif
+#ifndef H3_ATTN_PIPELINED
+#define H3_ATTN_PIPELINED 1        // 1: software-pipelined kernel, 0: simple kernel
 #endif
 
 namespace {
@@ -24,7 +28,8 @@ namespace {
 using namespace h3;
 
 constexpr int kRB = H3_ROWS_PER_WAVE_BLOCKS;
-constexpr int kBM = 4 * 32 * kRB;  // query rows per attention workgroup
+constexpr bool kPipelined = H3_ATTN_PIPELINED != 0;
+constexpr int kBM = kPipelined ? pipe::kRows : 4 * 32 * kRB;  // query rows per workgroup
 
 // ---------------------------------------------------------------- device check
 // Per-device verdict of "is this a gfx950": 0 unknown, 1 yes, 2 no.
@@ -216,10 +221,17 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
     aa.eps = eps;
     aa.rope = ra;
     const unsigned blocks = (unsigned)((int64_t)H * m_tiles);
-    if (norm)
-      attn_fwd_kernel<kRB, true><<<blocks, 256, 0, stream>>>(aa);
-    else
-      attn_fwd_kernel<kRB, false><<<blocks, 256, 0, stream>>>(aa);
+    if (kPipelined) {
+      if (norm)
+        attn_pipelined_kernel<true><<<blocks, pipe::kThreads, 0, stream>>>(aa);
+      else
+        attn_pipelined_kernel<false><<<blocks, pipe::kThreads, 0, stream>>>(aa);
+    } else {
+      if (norm)
+        attn_fwd_kernel<kRB, true><<<blocks, 256, 0, stream>>>(aa);
+      else
+        attn_fwd_kernel<kRB, false><<<blocks, 256, 0, stream>>>(aa);
+    }
     H3_TRY(launched());
   }
   return H3_OK;

@@ -64,9 +64,12 @@ struct ChunkRot {
   double pos;       // position along the chunk's axis
 };
 
+// Tokens past n_1d without a 3-axis layout (sections zero) only occur as query rows in
+// the buffer tail, whose results are discarded; they take the 1-D path so every table
+// index stays inside the 64 pairs.
 __device__ __forceinline__ ChunkRot chunk_rotation(const RopeArgs& r, int64_t token, int cc) {
   ChunkRot c;
-  if (token < r.n_1d) {
+  if (token < r.n_1d || r.sec[0] == 0) {
     c.three_axis = false;
     c.first = cc < 8;
     c.partner = cc ^ 8;
