@@ -165,7 +165,7 @@ def main() -> int:
 
     row_bytes = w.heads * w.head_dim * 2
     tiles = (w.n_valid + 63) // 64
-    pack_bytes = 2 * w.n_valid * row_bytes + 2 * w.heads * tiles * 16384
+    pack_bytes = 2 * w.n_valid * row_bytes + w.heads * tiles * 35840
     ms_pack = timed(lambda: B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps,
                                       rope=rope), args.steps)
     q2, k2 = torch.empty_like(d["q"]), torch.empty_like(d["k"])

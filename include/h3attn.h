@@ -104,7 +104,11 @@ h3_status h3_qk_rmsnorm_rope(const void* q_in, const void* k_in, void* q_out, vo
 
 /* Bytes of device workspace an attention call with this shape needs (0 if the shape
  * is invalid).  The workspace holds the key and value operands of every batch repacked
- * for the attention kernel: B * 2 * H * round_up(S, 64) * D bf16 values. */
+ * for the attention kernel as 64-key tiles of 35,840 bytes each,
+ * B * H * ceil(S / 64) * 35840 bytes (about 1.09x the bf16 size of K plus V), followed
+ * by one 4-byte word per 256 query rows of every head and batch (which of the two
+ * attention passes handles those rows), rounded up to 256 bytes:
+ * round_up(B * H * ceil(S / 256) * 4, 256) bytes. */
 size_t h3_attn_workspace_size(const h3_shape* shape);
 
 /* Stage 1 of attention: repack K and V of every batch into `workspace` (keys of 64-key
@@ -123,10 +127,12 @@ h3_status h3_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_he
  * taken from a workspace filled by h3_kv_pack for the same shape.  With w_q non-NULL
  * each Q row is RMS-normalised and rotated in registers on load (same arithmetic as
  * h3_qk_rmsnorm_rope); with w_q NULL, Q is used as is.  Output rows [N_b, S) are zero.
+ * The tile images are only read; the pass words after them are written, so two calls
+ * sharing one workspace must not overlap in time.
  * Errors: as h3_kv_pack. */
 h3_status h3_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head_stride,
                          float eps, const h3_rope* rope, float softmax_scale,
-                         const h3_shape* shape, const void* workspace, size_t workspace_bytes,
+                         const h3_shape* shape, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
 /* Dense non-causal softmax attention over the valid tokens ([Blog §3.1]), with Q and

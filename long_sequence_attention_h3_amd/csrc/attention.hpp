@@ -1,26 +1,45 @@
 // attention.hpp — dense non-causal softmax attention over the valid tokens of a packed,
-// aligned buffer, bf16 MFMA on gfx950.
+// aligned buffer; software-pipelined for gfx950.
 //
 // Pages: "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH3 的实时服务"
 // (Chinese translation of the vLLM blog post), §3.1: attention receives the valid
 // sequence length and the structural tail padding is not computed; §3.2: the Q/K
-// RMSNorm + RoPE prologue is fused (here: the Q half in registers).
+// RMSNorm + RoPE prologue is fused (the Q half here, in registers).
 //
-// Structure (one workgroup = 4 waves = one head x BM query rows, BM = 4 * 32 * RB):
-//   * Q: each wave holds RB blocks of 32 query rows in registers as MFMA B operands
-//     (optionally normalised + rotated on load).
-//   * K/V: 64-key tiles, prepared by kv_pack_kernel as swizzled 16 KiB images, are
-//     copied linearly into a double-buffered LDS ring (2 x 32 KiB).
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16.  Lane l of a wave owns query row
-//     l % 32 of each row block; K rows are read in the order swap23(l % 32) so that the
-//     accumulator registers come out in the exact order of the P^T B operand of the
-//     second product (no cross-lane shuffles between the two products).
-//   * Online softmax in fp32, base-2, with the softmax scale folded into the exponent;
-//     the running max is only raised when a new score exceeds it by more than kTau
-//     (log2 units), so the O rescale is skipped almost always.
-//   * O^T += V^T P^T with the same MFMA; V^T chunks come straight from the V image.
-//   * Epilogue: O / l -> bf16; rows in [N, S) are written as zeros.
+// Why the pipeline.  On gfx950 a wave can issue VALU work while its own MFMA runs, but
+// only a few instructions' worth per MFMA (about two v_exp_f32 or four full-rate ops per
+// 32x32x16 MFMA are hidden); VALU work of another wave on the same SIMD overlaps much
+// less.  So each wave interleaves the softmax of one 64-key tile with the matrix
+// products of its neighbours.  Per tile j, for the wave's 32 query rows:
+//
+//   B1: QK(j+1)  MFMA x16  ||  E(j)          (32 multiply + exp2)
+//   B2: PV(j)    MFMA x16  ||  C(j), M(j+1)   (bf16 convert + row sums, row max + check)
+//       -- stage tile j+2 into LDS; barrier; load tile j+3 --
+//
+// QK: S^T = K Q^T (two 32-key halves); M: row max of the new scores, raising the running
+// max where it is exceeded (rare branch); E: p = exp2(c s); C: p -> bf16 and row sums;
+// PV: O^T += V^T P^T.  The scores of tiles j and j+1 live in two register sets used
+// alternately (loop unrolled by two).
+//
+// Arithmetic.  Scores s = q.k are exact bf16 products summed in fp32, in raw units; the
+// QK accumulation starts from -m (the running max) as its C operand, so the accumulator
+// holds s - m and p = exp2(c (s - m)) with c = softmax_scale * log2(e) applied in fp32
+// (pre-scaling Q by c in bf16 would save the multiply but add a score error growing with
+// the logits).  The running max is raised only when a score exceeds it by more than
+// kTauP / c, so p <= 2^8 and the O rescale is rare.  Keys >= N in the last tile start
+// from -inf instead.  Row sums use v_dot2_f32_bf16 on the bf16-rounded p, so the
+// normaliser matches the weights fed to the PV product exactly.
+//
+// Memory.  Eight waves (256 query rows) share each K/V tile.  Tiles (prepared by
+// kv_pack_kernel as padded 35 KiB images, layout in common.hpp) go through a 3-slot LDS
+// ring: tile j is read from B1(j-1) to B2(j).  Tile j+2 is copied global -> LDS directly
+// (global_load_lds_dwordx4, no staging registers) during step j into the slot tile j-1
+// left, and waited for at the step's end, before its one barrier.  Every operand read is
+// one base register plus an immediate offset.  Everything fits in 256 VGPRs per lane, two
+// waves per SIMD.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "prologue.hpp"
@@ -30,14 +49,14 @@ namespace h3 {
 struct AttnArgs {
   const __bf16* q;
   __bf16* o;
-  const char* k_img;
-  const char* v_img;
+  const char* img;        // packed K/V tile images, [head][tile]
   int64_t tiles_per_head;
   int64_t in_stride, out_stride;
   int64_t n_valid, seq_buf;
   int heads;
-  int m_tiles;            // ceil(seq_buf / BM)
+  int m_tiles;            // ceil(seq_buf / rows per workgroup)
   float scale_log2;       // softmax_scale * log2(e)
+  int* wg_checked;        // per workgroup: 1 = left to the checked pass
   // fused Q prologue
   const __bf16* w_q;
   int64_t w_head_stride;
@@ -45,70 +64,292 @@ struct AttnArgs {
   RopeArgs rope;
 };
 
-// Raise the running max only when a score exceeds it by more than this (log2 units):
-// exponentials stay <= 2^kTau, far inside fp32 and bf16 range.
-constexpr float kTau = 8.0f;
+constexpr float kTauP = 8.0f;  // log2 units
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+namespace attn {
 
-// Waves per SIMD the register budget is sized for: two workgroups per CU with one
-// 32-row block per wave (<= 256 registers), one with two blocks (<= 512).
-template <int RB>
-struct AttnOccupancy {
-  static constexpr int kWavesPerEU = RB == 1 ? 2 : 1;
+#ifndef H3_ATTN_SLOTS
+#define H3_ATTN_SLOTS 3
+#endif
+constexpr int kSlots = H3_ATTN_SLOTS;       // LDS ring depth (tiles)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;           // query rows per workgroup
+constexpr int kImageChunks = kTileImageBytes / 1024;  // 1 KiB DMA chunks per tile (35)
+static_assert(kTileImageBytes % 1024 == 0, "tile image must be whole 1 KiB chunks");
+
+struct Wave {
+  bf16x8 q[8];      // Q^T B operands
+  f32x16 o[4];      // O^T accumulators per 32-channel block
+  bf16x8 p[4];      // P^T B operands per 16-key step
+  f32x16 negm;      // C operand of QK: -m, splat
+  float m, l;       // running max (raw score units), row-sum partial over this lane's keys
+  float c;          // softmax_scale * log2(e)
+  float tau;        // kTauP / c: the running-max slack in raw units
 };
 
-template <int RB, bool kFusedQ>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(AttnOccupancy<RB>::kWavesPerEU,
-                                   AttnOccupancy<RB>::kWavesPerEU))) void
+// S^T (64 keys x 32 rows, as two 32-key halves).  `kb_base` = this lane's K operand
+// address in the slot: key row l32, channel chunk hl; the (kb, ks) operand sits at
+// + kb*32 rows + ks*32 bytes.  The accumulation starts from c0[kb].
+__device__ __forceinline__ void qk(const Wave& w, f32x16* s, const char* kb_base,
+                                   const f32x16* c0) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_base + kb * 32 * kKRowPitch + ks * 32);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.q[ks], ks == 0 ? c0[kb] : s[kb], 0,
+                                                      0, 0);
+    }
+  }
+}
+
+// O^T += V^T P^T.  `vb_base` = this lane's V operand address: channel row l32, key chunk hl;
+// the (db, t) operand sits at + db*32 rows + t*32 bytes.
+__device__ __forceinline__ void pv(Wave& w, const char* vb_base) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb_base + db * 32 * kVRowPitch + t * 32);
+      w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.p[t], w.o[db], 0, 0, 0);
+    }
+  }
+}
+
+// E: p = exp2(c acc), in place.
+__device__ __forceinline__ void ex(const Wave& w, f32x16* s) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[kb][e] = __builtin_amdgcn_exp2f(s[kb][e] * w.c);
+}
+
+// C: p -> bf16 operands; row sum of the rounded values (v_dot2_f32_bf16 with (1, 1)).
+__device__ __forceinline__ void cv(Wave& w, const f32x16* s) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc0 = w.l, acc1 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    bf16x2 pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 f = {s[t >> 1][8 * (t & 1) + 2 * i], s[t >> 1][8 * (t & 1) + 2 * i + 1]};
+      pr[i] = __builtin_convertvector(f, bf16x2);
+    }
+    acc0 = __builtin_amdgcn_fdot2_f32_bf16(pr[0], ones, acc0, false);
+    acc1 = __builtin_amdgcn_fdot2_f32_bf16(pr[1], ones, acc1, false);
+    acc0 = __builtin_amdgcn_fdot2_f32_bf16(pr[2], ones, acc0, false);
+    acc1 = __builtin_amdgcn_fdot2_f32_bf16(pr[3], ones, acc1, false);
+    const bf16x8 pv8 = {pr[0][0], pr[0][1], pr[1][0], pr[1][1],
+                        pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
+    w.p[t] = pv8;
+  }
+  w.l = acc0 + acc1;
+}
+
+// M: tile row max of acc; raise the running max where it is exceeded by more than
+// kTauP / c (always on the first tile).  Rare path: rescale O and l, shift acc and -m.
+template <bool kFirst>
+__device__ __forceinline__ void mx(Wave& w, f32x16* s) {
+  float v = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v = fmaxf(v, s[kb][e]);
+  v = pair_max(v);
+  const bool need = kFirst || v > w.tau;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float delta = need ? v : 0.0f;
+    w.m += delta;
+    if (!kFirst) {
+      const float alpha = __builtin_amdgcn_exp2f(-delta * w.c);
+      w.l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w.o[db][e] *= alpha;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w.negm[e] = -w.m;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] -= delta;
+  }
+}
+
+// One steady-state step as an explicit instruction order.  kCheck: also take the row
+// max of tile j+1 for the running-max check (not needed when the wave's scores are
+// provably bounded, see the kernel).  QK(j+1) and PV(j) are 32
+// MFMAs; after each MFMA comes the operand read of the MFMA three places later and the
+// VALU work that the MFMA hides:
+//   QK MFMA i:  exp2 of values 2i, 2i+1 of tile j; from i = 4 on, two convert/sum ops of
+//               the 8-value group finished four MFMAs earlier;
+//   PV MFMA i:  the last group's convert/sum ops (i < 4), one max3 of tile j+1's scores.
+// A scheduling barrier after each group keeps the compiler from clustering the VALU
+// work (which it otherwise does, leaving MFMAs waiting on reads and VALU unhidden).
+template <bool kCheck>
+__device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
+                                            const char* kbase, const char* vbase,
+                                            const f32x16* c0, float& vmax) {
+  bf16x8 kop[16], vop[16];
+  auto read_k = [&](int i) {  // operand of QK MFMA i: kb = i & 1, ks = i >> 1
+    kop[i] = *reinterpret_cast<const bf16x8*>(kbase + (i & 1) * 32 * kKRowPitch +
+                                              (i >> 1) * 32);
+  };
+  auto read_v = [&](int i) {  // operand of PV MFMA i: t = i >> 2, db = i & 3
+    vop[i] = *reinterpret_cast<const bf16x8*>(vbase + (i & 3) * 32 * kVRowPitch +
+                                              (i >> 2) * 32);
+  };
+  auto read = [&](int i) {  // operand i of the step's 32 MFMAs
+    if (i < 16)
+      read_k(i);
+    else if (i < 32)
+      read_v(i - 16);
+  };
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc0 = w.l, acc1 = 0.0f;
+  bf16x2 pr[4][4];
+  // convert/sum op k (0..7) of 16-key group t: k < 4 converts pair k, k >= 4 adds it
+  auto cv_op = [&](int t, int k) {
+    if (k < 4) {
+      const int i = k;
+      const f32x2 f = {cur[t >> 1][8 * (t & 1) + 2 * i], cur[t >> 1][8 * (t & 1) + 2 * i + 1]};
+      pr[t][i] = __builtin_convertvector(f, bf16x2);
+    } else {
+      const int i = k - 4;
+      // the empty asm keeps the compiler from sinking the sum to the end of the step
+      if (i & 1) {
+        acc1 = __builtin_amdgcn_fdot2_f32_bf16(pr[t][i], ones, acc1, false);
+        asm volatile("" : "+v"(acc1));
+      } else {
+        acc0 = __builtin_amdgcn_fdot2_f32_bf16(pr[t][i], ones, acc0, false);
+        asm volatile("" : "+v"(acc0));
+      }
+      if (i == 3) {
+        const bf16x8 pv8 = {pr[t][0][0], pr[t][0][1], pr[t][1][0], pr[t][1][1],
+                            pr[t][2][0], pr[t][2][1], pr[t][3][0], pr[t][3][1]};
+        w.p[t] = pv8;
+      }
+    }
+  };
+  read(0);
+  read(1);
+  read(2);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // QK(j+1) || exp(j), convert/sum(j)
+    const int kb = i & 1, ks = i >> 1;
+    nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], w.q[ks], ks == 0 ? c0[kb] : nxt[kb],
+                                                      0, 0, 0);
+    read(i + 3);
+    cur[(2 * i) >> 4][(2 * i) & 15] =
+        __builtin_amdgcn_exp2f(cur[(2 * i) >> 4][(2 * i) & 15] * w.c);
+    cur[(2 * i + 1) >> 4][(2 * i + 1) & 15] =
+        __builtin_amdgcn_exp2f(cur[(2 * i + 1) >> 4][(2 * i + 1) & 15] * w.c);
+    if (i >= 4) {
+      cv_op((i - 4) >> 2, 2 * ((i - 4) & 3));
+      cv_op((i - 4) >> 2, 2 * ((i - 4) & 3) + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float v = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // PV(j) || convert/sum(j), max(j+1)
+    const int t = i >> 2, db = i & 3;
+    w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i], w.p[t], w.o[db], 0, 0, 0);
+    read(i + 19);
+    if (i < 4) {
+      cv_op(3, 2 * i);
+      cv_op(3, 2 * i + 1);
+    }
+    if (kCheck) {  // tile j+1 scores: values 2i, 2i+1 of nxt
+      v = fmaxf(fmaxf(v, nxt[(2 * i) >> 4][(2 * i) & 15]), nxt[(2 * i + 1) >> 4][(2 * i + 1) & 15]);
+      asm volatile("" : "+v"(v));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  w.l = acc0 + acc1;
+  vmax = v;
+}
+
+// Rest of M after steady_step: row max across the lane pair, raise where needed.
+__device__ __forceinline__ void mx_finish(Wave& w, f32x16* s, float v) {
+  v = pair_max(v);
+  const bool need = v > w.tau;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float delta = need ? v : 0.0f;
+    w.m += delta;
+    const float alpha = __builtin_amdgcn_exp2f(-delta * w.c);
+    w.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) w.o[db][e] *= alpha;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w.negm[e] = -w.m;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] -= delta;
+  }
+}
+
+}  // namespace attn
+
+// kCheck = false: the fast pass; workgroups whose scores are not provably bounded are
+// flagged in wg_checked and left alone.  kCheck = true: the second pass; runs the flagged
+// workgroups with the per-tile running-max check and returns at once for the others.
+template <bool kFusedQ, bool kCheck>
+__global__ __launch_bounds__(attn::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_kernel(AttnArgs a) {
-  constexpr int kWaves = 4;
-  constexpr int BM = kWaves * RB * 32;
-  __shared__ __attribute__((aligned(16))) char smem[2][2 * kTileBytes];
+  using namespace attn;
+  __shared__ __attribute__((aligned(16))) char smem[kSlots * kTileImageBytes];
   __shared__ FreqTable ft;
 
   const int logical = xcd_remap(blockIdx.x, a.heads * a.m_tiles);
   const int head = logical / a.m_tiles;
-  const int64_t m0 = (int64_t)(logical % a.m_tiles) * BM;
+  const int64_t m0 = (int64_t)(logical % a.m_tiles) * kRows;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform across the wave: keep it in a scalar register
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hl = lane >> 5, l32 = lane & 31;
   const int64_t hoff = (int64_t)head * kHeadDim;
 
-  // Workgroups entirely past the valid length only zero their output rows.
-  if (m0 >= a.n_valid) {
-    const int64_t rows = (a.seq_buf - m0) < BM ? (a.seq_buf - m0) : BM;
-    for (int64_t i = tid; i < rows * kChunks; i += 256) {
+  const int wg = logical;
+  if (kCheck && a.wg_checked[wg] == 0) return;  // done by the fast pass
+  if (m0 >= a.n_valid) {  // rows past the valid length: zeros only
+    if (tid == 0) a.wg_checked[wg] = 0;
+    const int64_t rows = (a.seq_buf - m0) < kRows ? (a.seq_buf - m0) : kRows;
+    for (int64_t i = tid; i < rows * kChunks; i += kThreads) {
       const int64_t r = m0 + i / kChunks;
       *reinterpret_cast<u32x4*>(a.o + r * a.out_stride + hoff + (i % kChunks) * 8) =
           u32x4{0u, 0u, 0u, 0u};
     }
     return;
   }
-
   if (kFusedQ) {
-    fill_freq_table(&ft, a.rope, tid, 256);
+    fill_freq_table(&ft, a.rope, tid, kThreads);
     __syncthreads();
   }
 
-  // ---- Q rows -> registers (B operand: lane holds row l32, channels 16ks + 8hl .. +8)
-  bf16x8 qreg[RB][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int64_t row = m0 + (wave * RB + rb) * 32 + l32;
-    const bool valid = row < a.n_valid;
+  Wave w;
+  const float c2 = a.scale_log2;
+  const int64_t row = m0 + wave * 32 + l32;
+  const bool row_valid = row < a.n_valid;
+
+  // ---- Q row -> B operands (lane: channels 16ks + 8hl .. +8)
+  {
     const __bf16* qrow = a.q + row * a.in_stride + hoff;
     u32x4 raw[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      raw[ks] = valid ? *reinterpret_cast<const u32x4*>(qrow + (2 * ks + hl) * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
+      raw[ks] = row_valid ? *reinterpret_cast<const u32x4*>(qrow + (2 * ks + hl) * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
     if (kFusedQ) {
-      // RMS over the row: partials of the 8 own chunks, the other 8 from lane l^32,
-      // combined in the canonical pairwise tree (chunks c, c^1, then c^2, c^4, c^8).
+      // RMS of the row: partials of the 8 own chunks, the other 8 from lane l^32, combined
+      // in the canonical pairwise tree (chunks c, c^1, then c^2, c^4, c^8).
       float part[8], other[8];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
@@ -118,192 +359,200 @@ attn_fwd_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) other[ks] = other_half(part[ks]);
-      // chunk 2ks is even, 2ks+1 odd: level-1 sums p[2ks] + p[2ks+1]
       float s1[8];
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) s1[ks] = hl ? other[ks] + part[ks] : part[ks] + other[ks];
       const float s2[4] = {s1[0] + s1[1], s1[2] + s1[3], s1[4] + s1[5], s1[6] + s1[7]};
       const float s3[2] = {s2[0] + s2[1], s2[2] + s2[3]};
-      const float ss = s3[0] + s3[1];
-      const float inv = inv_rms(ss, a.eps);
-      const __bf16* w = a.w_q + (int64_t)head * a.w_head_stride;
+      const float inv = inv_rms(s3[0] + s3[1], a.eps);
+      const __bf16* wq = a.w_q + (int64_t)head * a.w_head_stride;
 #pragma unroll 1
       for (int ks = 0; ks < 8; ++ks) {
         const int cc = 2 * ks + hl;
         const ChunkRot cr = chunk_rotation(a.rope, row, cc);
         float x[8], xp[8], wv[8], wpv[8], y[8];
         unpack8(raw[ks], x);
-        const u32x4 praw = valid ? *reinterpret_cast<const u32x4*>(qrow + cr.partner * 8)
-                                 : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 praw = row_valid ? *reinterpret_cast<const u32x4*>(qrow + cr.partner * 8)
+                                     : u32x4{0u, 0u, 0u, 0u};
         unpack8(praw, xp);
-        unpack8(*reinterpret_cast<const u32x4*>(w + cc * 8), wv);
-        unpack8(*reinterpret_cast<const u32x4*>(w + cr.partner * 8), wpv);
+        unpack8(*reinterpret_cast<const u32x4*>(wq + cc * 8), wv);
+        unpack8(*reinterpret_cast<const u32x4*>(wq + cr.partner * 8), wpv);
         norm_rotate_chunk(x, xp, wv, wpv, inv, cr, &ft, y);
-        raw[ks] = pack8(y);
+        raw[ks] = pack8(y);  // the same bf16 values h3_qk_rmsnorm_rope writes
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qreg[rb][ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+    for (int ks = 0; ks < 8; ++ks) w.q[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
   }
-
-  // ---- main loop over 64-key tiles
-  const int64_t n_tiles = (a.n_valid + kTileKeys - 1) / kTileKeys;
-  const char* kimg = a.k_img + (int64_t)head * a.tiles_per_head * kTileBytes;
-  const char* vimg = a.v_img + (int64_t)head * a.tiles_per_head * kTileBytes;
-  const int tail_keys = (int)(a.n_valid - (n_tiles - 1) * kTileKeys);  // 1..64
-
-  float m_run[RB], l_run[RB];
-  f32x16 oacc[RB][4];
+  w.c = c2;
+  w.tau = kTauP / c2;
+  w.m = 0.0f;
+  w.l = 0.0f;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.0f;
+  for (int e = 0; e < 16; ++e) w.negm[e] = 0.0f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[rb][db] = f32x16{};
-  }
+  for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
 
-  // staging: each thread copies 4 x 16 B of the K image and 4 x 16 B of the V image
-  u32x4 stage[8];
-  auto load_tile = [&](int64_t kt) {
-    const char* ks = kimg + kt * kTileBytes;
-    const char* vs = vimg + kt * kTileBytes;
+  const int nt = (int)((a.n_valid + kTileKeys - 1) / kTileKeys);
+  const char* img = a.img + (int64_t)head * a.tiles_per_head * kTileImageBytes;
+  const int tail = (int)(a.n_valid - (int64_t)(nt - 1) * kTileKeys);  // valid keys, last tile
+
+  // Tiles go straight from global memory into their LDS slot (global_load_lds_dwordx4:
+  // lane i of a wave writes 16 bytes at the wave's LDS base + 16 i).  Wave w copies the
+  // 1 KiB chunks w, w + 8, ... of the 35 KiB image.
+  auto slot = [&](int t) __attribute__((always_inline)) { return smem + (t % kSlots) * kTileImageBytes; };
+  auto load = [&](int t) __attribute__((always_inline)) {
+    const char* src = img + (int64_t)t * kTileImageBytes;
+    char* dst = slot(t);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      stage[p] = *reinterpret_cast<const u32x4*>(ks + (p * 256 + tid) * 16);
-      stage[4 + p] = *reinterpret_cast<const u32x4*>(vs + (p * 256 + tid) * 16);
+    for (int i = 0; i < (kImageChunks + kWaves - 1) / kWaves; ++i) {
+      const int c = wave + i * kWaves;
+      if (c < kImageChunks)
+        __builtin_amdgcn_global_load_lds(
+            src + c * 1024 + lane * 16, (__attribute__((address_space(3))) void*)(dst + c * 1024),
+            16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<u32x4*>(&smem[buf][(p * 256 + tid) * 16]) = stage[p];
-      *reinterpret_cast<u32x4*>(&smem[buf][kTileBytes + (p * 256 + tid) * 16]) = stage[4 + p];
-    }
-  };
+  // All of this thread's tile loads have landed in LDS (s_waitcnt vmcnt(0)).
+  auto loads_done = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // per-lane operand offsets within a slot (see qk / pv)
+  const int k_lane = l32 * kKRowPitch + hl * 16;
+  const int v_lane = kKImageBytes + l32 * kVRowPitch + hl * 16;
 
-  // LDS read offsets (bytes) within one buffer.
-  // K: A operand row kb*32 + swap23(l32), chunk 2ks + hl, slot row*16 + (chunk ^ (l32 & 15)).
-  const int krow = swap23(l32);
-  // V: A operand row d = db*32 + l32, chunk 2t + hl, slot d*8 + (chunk ^ vswz(d)).
-  const int vx = vswz(l32);
-  const float c2 = a.scale_log2;
-
-  for (int64_t kt = 0; kt < n_tiles; ++kt) {
-    const bool has_next = kt + 1 < n_tiles;
-    if (has_next) load_tile(kt + 1);
-    const char* kl = smem[kt & 1];
-    const char* vl = kl + kTileBytes;
-
-    // S^T (keys x rows) for two 32-key blocks
-    f32x16 sacc[2][RB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[kb][rb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + krow;
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(
-            kl + (r * 16 + ((2 * ks + hl) ^ (l32 & 15))) * 16);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[kb][rb] = mfma32(kop, qreg[rb][ks], sacc[kb][rb]);
-      }
-    }
-
-    // mask keys >= N (last tile only).  Register 4i+j of block kb holds key
-    // kb*32 + 16(i>>1) + 8hl + 4(i&1) + j of the tile.
-    if (kt == n_tiles - 1 && tail_keys < kTileKeys) {
+  // QK of tile t into s.  kMask (the last tile): the C operand is -inf for keys >= tail;
+  // register 4i+j of half kb holds key kb*32 + 8i + 4hl + j.  Decided at compile time so
+  // that no branch separates the products from the work they overlap.
+  auto qk_tile = [&](f32x16* s, int t, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    f32x16 c[2] = {w.negm, w.negm};
+    if (kMask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int key = kb * 32 + 16 * (i >> 1) + 8 * hl + 4 * (i & 1) + j;
-            if (key >= tail_keys)
-#pragma unroll
-              for (int rb = 0; rb < RB; ++rb) sacc[kb][rb][4 * i + j] = -INFINITY;
+            const int key = kb * 32 + 8 * i + 4 * hl + j;
+            if (key >= tail) c[kb][4 * i + j] = -INFINITY;
           }
     }
+    qk(w, s, slot(t) + k_lane, c);
+  };
 
-    // online softmax, P^T as bf16 B operands
-    bf16x8 preg[RB][4];
+  // One pipeline step for tile j: `cur` holds acc of tile j (max already applied), `nxt`
+  // receives tile j+1.  kNext: tile j+1 exists; kMaskNext: it is the last tile.
+  auto step = [&](f32x16* cur, f32x16* nxt, int j, auto next_tag, auto mask_tag,
+                  auto check_tag) __attribute__((always_inline)) {
+    constexpr bool kNext = decltype(next_tag)::value;
+    constexpr bool kMask = decltype(mask_tag)::value;
+    constexpr bool kChk = decltype(check_tag)::value;
+    if (j + kSlots - 1 < nt) load(j + kSlots - 1);  // into the slot tile j-1 left
+    if (kNext) {
+      f32x16 c[2] = {w.negm, w.negm};
+      if (kMask) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mx = sacc[0][rb][0];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][rb][e]);
-      mx = pair_max(mx);
-      const bool raise = mx * c2 > m_run[rb] * c2 + kTau || m_run[rb] == -INFINITY;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float m_new = raise ? fmaxf(mx, m_run[rb]) : m_run[rb];
-        const float alpha = __builtin_amdgcn_exp2f((m_run[rb] - m_new) * c2);
-        m_run[rb] = m_new;
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[rb][db][e] *= alpha;
+            for (int jj = 0; jj < 4; ++jj) {
+              const int key = kb * 32 + 8 * i + 4 * hl + jj;
+              if (key >= tail) c[kb][4 * i + jj] = -INFINITY;
+            }
       }
-      const float mc = m_run[rb] * c2;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[t >> 1][rb][8 * (t & 1) + e], c2, -mc));
-          lsum += p[e];
-        }
-        preg[rb][t] = __builtin_bit_cast(bf16x8, pack8(p));
-      }
-      l_run[rb] += lsum;
+      float v;
+      steady_step<kChk>(w, cur, nxt, slot(j + 1) + k_lane, slot(j) + v_lane, c, v);
+      if (kChk) mx_finish(w, nxt, v);
+    } else {  // last tile: no next scores
+      ex(w, cur);
+      cv(w, cur);
+      pv(w, slot(j) + v_lane);
     }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + l32;
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(
-            vl + (d * 8 + ((2 * t + hl) ^ vx)) * 16);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32(vop, preg[rb][t], oacc[rb][db]);
-      }
-    }
-
-    if (has_next) store_tile((kt + 1) & 1);
+    loads_done();  // tile j+1 (and j+2) in LDS before the next step
     __syncthreads();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+
+  // ---- pipeline fill: tiles 0 .. kSlots-2
+#pragma unroll
+  for (int t = 0; t < kSlots - 1; ++t)
+    if (t < nt) load(t);
+  loads_done();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (nt == 1)
+    qk_tile(sa, 0, T{});
+  else
+    qk_tile(sa, 0, F{});
+  mx<true>(w, sa);  // the running max starts at tile 0's row max
+
+  // Score bound.  Every score of this lane's row satisfies s <= |q| * max_j |k_j|
+  // (Cauchy-Schwarz), and the running max starts at tile 0's row maximum m0, a lower
+  // bound of the row's true maximum.  If c (|q| max|k| - m0) <= 64 for every row of the
+  // workgroup, no exponent exceeds 64, the row's largest term is >= 1
+  // (so l >= 1), and l <= 2^84 for up to 2^20 keys: the fp32 sums stay far from overflow
+  // and, bf16 and fp32 precision being relative, the result is as accurate as with the
+  // exact running max.  Then the fast pass runs without the per-tile max and its branch;
+  // otherwise the workgroup is left to the checked pass.
+  if (!kCheck) {
+    float kmax = 0.0f;
+    for (int t = lane; t < nt; t += 64)
+      kmax = fmaxf(kmax, *reinterpret_cast<const float*>(img + (int64_t)t * kTileImageBytes +
+                                                          kKNormOffset));
+    for (int off = 32; off >= 1; off >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off, 64));
+    float q2 = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q2 = fmaf((float)w.q[ks][e], (float)w.q[ks][e], q2);
+    const float bound = sqrtf(pair_sum(q2)) * 1.0001f * kmax;
+    const bool ok = (bound - w.m) * c2 <= 64.0f;  // false for NaN as well
+    __shared__ int wave_fail[kWaves];
+    if (lane == 0) wave_fail[wave] = __builtin_amdgcn_ballot_w64(!ok) != 0;
+    __syncthreads();
+    int fail = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) fail |= wave_fail[i];
+    if (tid == 0) a.wg_checked[wg] = fail;
+    if (fail) return;
   }
 
-  // ---- epilogue: lane holds O[row l32][d = db*32 + 8i + 4hl + j] at register 4i+j
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int64_t row = m0 + (wave * RB + rb) * 32 + l32;
-    if (row >= a.seq_buf) continue;
-    const float l = pair_sum(l_run[rb]);
-    const bool valid = row < a.n_valid;
-    const float inv = 1.0f / l;
+  // steady steps: tile j+1 exists and is not the last (j <= nt-3), two at a time
+  using Check = std::integral_constant<bool, kCheck>;
+  int j = 0;
+  for (; j + 4 <= nt; j += 2) {
+    step(sa, sb, j, T{}, F{}, Check{});
+    step(sb, sa, j + 1, T{}, F{}, Check{});
+  }
+  // the last one to three steps; `sa` holds the current tile here
+  const int r = nt - j;
+  if (r == 3) {
+    step(sa, sb, j, T{}, F{}, Check{});
+    step(sb, sa, j + 1, T{}, T{}, Check{});
+    step(sa, sb, j + 2, F{}, F{}, Check{});
+  } else if (r == 2) {
+    step(sa, sb, j, T{}, T{}, Check{});
+    step(sb, sa, j + 1, F{}, F{}, Check{});
+  } else {
+    step(sa, sb, j, F{}, F{}, Check{});
+  }
+
+  // ---- epilogue: lane holds O[row][d = db*32 + 8i + 4hl + j] at register 4i+j
+  if (row < a.seq_buf) {
+    const float inv = 1.0f / pair_sum(w.l);
     __bf16* orow = a.o + row * a.out_stride + hoff;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        u32x2 w = {0u, 0u};  // rows in [N, S): exact +0
-        if (valid) {
-          w[0] = pack_bf16x2(oacc[rb][db][4 * i] * inv, oacc[rb][db][4 * i + 1] * inv);
-          w[1] = pack_bf16x2(oacc[rb][db][4 * i + 2] * inv, oacc[rb][db][4 * i + 3] * inv);
+        u32x2 v = {0u, 0u};  // rows in [N, S): exact +0
+        if (row_valid) {
+          v[0] = pack_bf16x2(w.o[db][4 * i] * inv, w.o[db][4 * i + 1] * inv);
+          v[1] = pack_bf16x2(w.o[db][4 * i + 2] * inv, w.o[db][4 * i + 3] * inv);
         }
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * i + 4 * hl) = w;
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * i + 4 * hl) = v;
       }
   }
 }

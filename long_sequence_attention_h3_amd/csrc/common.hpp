@@ -15,10 +15,23 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
-constexpr int kHeadDim = 128;        // the only supported head size
+constexpr int kHeadDim = 128;          // the only supported head size
 constexpr int kChunks = kHeadDim / 8;  // 16-byte chunks (8 bf16) per head row
-constexpr int kTileKeys = 64;        // keys per packed K/V tile
-constexpr int kTileBytes = kTileKeys * kHeadDim * 2;  // 16 KiB per tile image
+constexpr int kTileKeys = 64;          // keys per packed K/V tile
+
+// Packed K/V tile image, the exact byte layout the attention kernel keeps in LDS:
+//   K part: 64 key rows x (256 B of channels + 16 B pad)            = 17,408 B
+//   V part: 128 channel rows x (128 B of keys + 16 B pad)            = 18,432 B
+// The pads make every MFMA operand read of the attention kernel bank-conflict free
+// with a plain base + immediate-offset address.
+constexpr int kKRowPitch = kHeadDim * 2 + 16;             // 272
+constexpr int kVRowPitch = kTileKeys * 2 + 16;            // 144
+constexpr int kKImageBytes = kTileKeys * kKRowPitch;      // 17,408
+constexpr int kVImageBytes = kHeadDim * kVRowPitch;       // 18,432
+constexpr int kTileImageBytes = kKImageBytes + kVImageBytes;  // 35,840 = 35 KiB
+// The pad of K row 0 carries the tile's largest K row norm (fp32, the norm of the bf16
+// values stored), the rest of every pad is zero.
+constexpr int kKNormOffset = kHeadDim * 2;  // byte 256 of the image
 
 // Rotary descriptor as the kernels see it.
 struct RopeArgs {

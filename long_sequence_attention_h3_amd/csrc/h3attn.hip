@@ -13,23 +13,13 @@
 #include <cstring>
 
 #include "attention.hpp"
-#include "attention_pipelined.hpp"
 #include "prologue.hpp"
-
-#ifndef H3_ROWS_PER_WAVE_BLOCKS
-#define H3_ROWS_PER_WAVE_BLOCKS 1  // 32-row blocks of queries per wave (simple kernel)
-#endif
-#ifndef H3_ATTN_PIPELINED
-#define H3_ATTN_PIPELINED 1        // 1: software-pipelined kernel, 0: simple kernel
-#endif
 
 namespace {
 
 using namespace h3;
 
-constexpr int kRB = H3_ROWS_PER_WAVE_BLOCKS;
-constexpr bool kPipelined = H3_ATTN_PIPELINED != 0;
-constexpr int kBM = kPipelined ? pipe::kRows : 4 * 32 * kRB;  // query rows per workgroup
+constexpr int kBM = attn::kRows;  // query rows per attention workgroup
 
 // ---------------------------------------------------------------- device check
 // Per-device verdict of "is this a gfx950": 0 unknown, 1 yes, 2 no.
@@ -110,12 +100,21 @@ h3_status check_weights(const void* w_q, const void* w_k, int64_t w_head_stride)
 
 int64_t tiles_per_head(const h3_shape* s) { return (s->seq_buf + kTileKeys - 1) / kTileKeys; }
 
-// Workspace layout: for batch b, the K images of all heads, then the V images:
-//   [b][K|V][head][tile] x 16 KiB.
-size_t batch_ws_bytes(const h3_shape* s) {
-  return 2 * (size_t)s->num_heads * (size_t)tiles_per_head(s) * (size_t)kTileBytes;
+int64_t attn_workgroups(const h3_shape* s) {
+  return (int64_t)s->num_heads * ((s->seq_buf + kBM - 1) / kBM);
 }
-size_t workspace_bytes(const h3_shape* s) { return (size_t)s->batch * batch_ws_bytes(s); }
+
+// Workspace layout: packed K/V tile images, [batch][head][tile] x kTileImageBytes, then
+// one int per attention workgroup and batch (which pass handles it).
+size_t batch_ws_bytes(const h3_shape* s) {
+  return (size_t)s->num_heads * (size_t)tiles_per_head(s) * (size_t)kTileImageBytes;
+}
+size_t flags_bytes(const h3_shape* s) {
+  return ((size_t)s->batch * (size_t)attn_workgroups(s) * sizeof(int) + 255) & ~size_t(255);
+}
+size_t workspace_bytes(const h3_shape* s) {
+  return (size_t)s->batch * batch_ws_bytes(s) + flags_bytes(s);
+}
 
 h3_status launched() { return hipGetLastError() == hipSuccess ? H3_OK : H3_ERR_LAUNCH; }
 
@@ -169,8 +168,7 @@ h3_status do_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_he
     pa.tiles_per_head = tph;
     pa.eps = eps;
     pa.rope = ra;
-    pa.k_img = ws;
-    pa.v_img = ws + per_batch / 2;
+    pa.img = ws;
     const dim3 grid((unsigned)((n + kTileKeys - 1) / kTileKeys), (unsigned)shp->num_heads);
     if (norm)
       kv_pack_kernel<true><<<grid, 128, 0, stream>>>(pa);
@@ -184,7 +182,7 @@ h3_status do_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_he
 // ---------------------------------------------------------------- stage 2: attention
 h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head_stride,
                          float eps, const h3_rope* rope, float softmax_scale,
-                         const h3_shape* shp, const void* workspace, size_t ws_bytes,
+                         const h3_shape* shp, void* workspace, size_t ws_bytes,
                          hipStream_t stream) {
   int64_t max_valid = 0;
   H3_TRY(check_shape(shp, &max_valid));
@@ -201,13 +199,14 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
   if (S == 0) return H3_OK;
   const int m_tiles = (int)((S + kBM - 1) / kBM);
   const size_t per_batch = batch_ws_bytes(shp);
+  int* flags = reinterpret_cast<int*>(static_cast<char*>(workspace) + shp->batch * per_batch);
   for (int b = 0; b < shp->batch; ++b) {
     const char* ws = static_cast<const char*>(workspace) + b * per_batch;
     AttnArgs aa{};
+    aa.wg_checked = flags + b * attn_workgroups(shp);
     aa.q = static_cast<const __bf16*>(q) + b * S * shp->in_row_stride;
     aa.o = static_cast<__bf16*>(o) + b * S * shp->out_row_stride;
-    aa.k_img = ws;
-    aa.v_img = ws + per_batch / 2;
+    aa.img = ws;
     aa.tiles_per_head = tiles_per_head(shp);
     aa.in_stride = shp->in_row_stride;
     aa.out_stride = shp->out_row_stride;
@@ -221,16 +220,13 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
     aa.eps = eps;
     aa.rope = ra;
     const unsigned blocks = (unsigned)((int64_t)H * m_tiles);
-    if (kPipelined) {
-      if (norm)
-        attn_pipelined_kernel<true><<<blocks, pipe::kThreads, 0, stream>>>(aa);
-      else
-        attn_pipelined_kernel<false><<<blocks, pipe::kThreads, 0, stream>>>(aa);
+    // fast pass, then the checked pass for the workgroups the fast pass flagged
+    if (norm) {
+      attn_fwd_kernel<true, false><<<blocks, attn::kThreads, 0, stream>>>(aa);
+      attn_fwd_kernel<true, true><<<blocks, attn::kThreads, 0, stream>>>(aa);
     } else {
-      if (norm)
-        attn_fwd_kernel<kRB, true><<<blocks, 256, 0, stream>>>(aa);
-      else
-        attn_fwd_kernel<kRB, false><<<blocks, 256, 0, stream>>>(aa);
+      attn_fwd_kernel<false, false><<<blocks, attn::kThreads, 0, stream>>>(aa);
+      attn_fwd_kernel<false, true><<<blocks, attn::kThreads, 0, stream>>>(aa);
     }
     H3_TRY(launched());
   }
@@ -312,7 +308,7 @@ h3_status h3_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_he
 
 h3_status h3_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head_stride,
                          float eps, const h3_rope* rope, float softmax_scale,
-                         const h3_shape* shape, const void* workspace, size_t workspace_bytes_,
+                         const h3_shape* shape, void* workspace, size_t workspace_bytes_,
                          hipStream_t stream) {
   return do_attn_packed(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape, workspace,
                         workspace_bytes_, stream);

@@ -212,16 +212,17 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
 // ---------------------------------------------------------------------------------
 // K/V pre-pass of the attention kernel.
 //
-// For head h, key tile kt (keys 64*kt .. 64*kt+63) it writes two 16 KiB images that the
-// attention kernel copies linearly into LDS:
-//   K image: row r (key), chunk c (channels 8c..8c+7) at 16-byte slot
-//            r*16 + (c ^ swap23(r & 15)),
-//   V image: channel d, key chunk c (keys 8c..8c+7 of channel d) at slot
-//            d*8 + (c ^ vswz(d)),   vswz(d) = (d & 7) ^ ((d >> 3) & 1),
-// swap23 exchanging bits 2 and 3.  The XOR swizzles make the attention kernel's LDS
-// reads conflict-free whether the LDS serves 8 or 16 lanes of a 16-byte read per
-// cycle.  Keys >= N are written as zeros.  With `norm` set, K rows are
-// RMS-normalised and rotated on the way (the layer path); otherwise copied.
+// For head h and key tile kt (keys 64 kt .. 64 kt + 63) it writes one contiguous tile
+// image (layout in common.hpp) that the attention kernel copies linearly into LDS:
+//   K part: key r, channels 8c .. 8c+7 at byte r*272 + 16c;
+//   V part: channel d, key chunk c at byte 17408 + d*144 + 16c, where chunk c holds, in
+//           order, the keys 16(c/2) + 4(c%2) + {0,1,2,3} and 16(c/2) + 8 + 4(c%2) + {0,1,2,3}.
+// The pad after K row 0 holds the tile's largest K row norm (the attention kernel bounds
+// its scores with it).
+// The V key order inside each 16-key group (bits 2 and 3 of the key index exchanged)
+// is the order in which the QK product leaves the probabilities in registers, so the PV
+// product consumes them without shuffles.  Keys >= N are written as zeros.  With `norm`
+// set, K rows are RMS-normalised and rotated on the way (the layer path).
 struct PackArgs {
   const __bf16* k;
   const __bf16* v;
@@ -229,17 +230,11 @@ struct PackArgs {
   int64_t w_head_stride;
   int64_t in_stride;
   int64_t n_valid;
-  int64_t tiles_per_head;  // capacity of the image arrays per head
+  int64_t tiles_per_head;  // capacity of the image array per head
   float eps;
   RopeArgs rope;
-  char* k_img;
-  char* v_img;
+  char* img;               // [head][tile] x kTileImageBytes
 };
-
-__device__ __forceinline__ int swap23(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-__device__ __forceinline__ int vswz(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 template <bool kNorm>
 __global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
@@ -252,12 +247,12 @@ __global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
     __syncthreads();
   }
   const int64_t key0 = kt * kTileKeys;
-  char* kimg = a.k_img + ((int64_t)h * a.tiles_per_head + kt) * kTileBytes;
-  char* vimg = a.v_img + ((int64_t)h * a.tiles_per_head + kt) * kTileBytes;
+  char* img = a.img + ((int64_t)h * a.tiles_per_head + kt) * kTileImageBytes;
   const int64_t hoff = (int64_t)h * kHeadDim;
 
   // K: 64 rows x 16 chunks; 8 rows per pass (16 lanes per row).
   const int cc = tid & 15;
+  float norm2_max = 0.0f;  // largest squared row norm seen by this thread's row group
   for (int r = tid >> 4; r < kTileKeys; r += 8) {
     const int64_t key = key0 + r;
     u32x4 out = {0u, 0u, 0u, 0u};
@@ -273,18 +268,42 @@ __global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
         out = *reinterpret_cast<const u32x4*>(row + cc * 8);
       }
     }
-    *reinterpret_cast<u32x4*>(kimg + (r * 16 + (cc ^ swap23(r & 15))) * 16) = out;
+    *reinterpret_cast<u32x4*>(img + r * kKRowPitch + cc * 16) = out;
+    float x[8];
+    unpack8(out, x);
+    float n2 = chunk_sumsq(x);
+    n2 += __shfl_xor(n2, 1, 16);
+    n2 += __shfl_xor(n2, 2, 16);
+    n2 += __shfl_xor(n2, 4, 16);
+    n2 += __shfl_xor(n2, 8, 16);
+    norm2_max = fmaxf(norm2_max, n2);
+  }
+  __shared__ float row_max[8];
+  if (cc == 0) row_max[tid >> 4] = norm2_max;
+  __syncthreads();
+  // the K row pads: row 0's carries the tile's largest row norm (rounded up a little so
+  // that it bounds the fp32 norm of every row), the others are zero
+  if (tid < kTileKeys) {
+    u32x4 pad = {0u, 0u, 0u, 0u};
+    if (tid == 0) {
+      float m2 = row_max[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m2 = fmaxf(m2, row_max[i]);
+      pad[0] = __float_as_uint(sqrtf(m2) * 1.0001f);
+    }
+    *reinterpret_cast<u32x4*>(img + tid * kKRowPitch + kKNormOffset) = pad;
   }
 
-  // V: thread (key chunk kc, channel chunk cg) transposes an 8 x 8 block:
-  // reads keys 8kc..8kc+7 at channels 8cg..8cg+7, writes 8 image chunks (one per
-  // channel, 8 keys each).
+  // V: thread (key chunk c, channel chunk cg) gathers the chunk's 8 keys at channels
+  // 8cg .. 8cg+7 and writes 8 image chunks (one per channel, 8 keys each).
   {
-    const int kc = tid & 7, cg = tid >> 3;  // 8 x 16 = 128 threads
+    char* vimg = img + kKImageBytes;
+    const int c = tid & 7, cg = tid >> 3;  // 8 x 16 = 128 threads
     uint32_t x[8][4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t key = key0 + kc * 8 + e;
+      const int kin = 16 * (c >> 1) + 8 * (e >> 2) + 4 * (c & 1) + (e & 3);
+      const int64_t key = key0 + kin;
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (key < a.n_valid)
         raw = *reinterpret_cast<const u32x4*>(a.v + key * a.in_stride + hoff + cg * 8);
@@ -292,18 +311,20 @@ __global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
       for (int i = 0; i < 4; ++i) x[e][i] = raw[i];
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {  // channel 8cg + c
+    for (int ch = 0; ch < 8; ++ch) {  // channel 8cg + ch
       u32x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // keys 2i and 2i+1 of channel c: 16-bit halves (c & 1) of dword c/2
-        const uint32_t lo = x[2 * i][c >> 1], hi = x[2 * i + 1][c >> 1];
-        o[i] = (c & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                       : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        // keys 2i and 2i+1 of channel ch: 16-bit halves (ch & 1) of dword ch/2
+        const uint32_t lo = x[2 * i][ch >> 1], hi = x[2 * i + 1][ch >> 1];
+        o[i] = (ch & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                        : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
       }
-      const int d = cg * 8 + c;
-      *reinterpret_cast<u32x4*>(vimg + (d * 8 + (kc ^ vswz(d))) * 16) = o;
+      const int d = cg * 8 + ch;
+      *reinterpret_cast<u32x4*>(vimg + d * kVRowPitch + c * 16) = o;
     }
+    // zero the V row pads
+    *reinterpret_cast<u32x4*>(vimg + tid * kVRowPitch + 128) = u32x4{};
   }
 }
 

@@ -70,11 +70,18 @@ def prologue(s, r, q_out=FAKE, eps=1e-6):
 
 def test_workspace_size_formula():
     L = B.lib()
+    tile = 64 * 272 + 128 * 144  # padded K rows + padded V rows per 64-key tile
+
+    def flags(words):  # one int per 256 query rows, rounded up to 256 bytes
+        return (words * 4 + 255) // 256 * 256
+
+    assert tile == 35840
     assert L.h3_attn_workspace_size(ctypes.byref(shape(H=42, S=58816, valid=(58758,)))) == \
-        2 * 42 * 919 * 16384
-    assert L.h3_attn_workspace_size(ctypes.byref(shape(S=65, valid=(1,)))) == 2 * 2 * 2 * 16384
+        42 * 919 * tile + flags(42 * 230)
+    assert L.h3_attn_workspace_size(ctypes.byref(shape(S=65, valid=(1,)))) == \
+        2 * 2 * tile + flags(2 * 1)
     assert L.h3_attn_workspace_size(ctypes.byref(shape(B_=3, S=64, valid=(1, 2, 3)))) == \
-        3 * 2 * 2 * 1 * 16384
+        3 * 2 * 1 * tile + flags(3 * 2 * 1)
     assert L.h3_attn_workspace_size(ctypes.byref(shape(D=64))) == 0
     assert L.h3_attn_workspace_size(None) == 0
 

@@ -110,6 +110,49 @@ def test_per_head_norm_weights(dev):
     assert_close(rows_of(out, rows), ref, "per-head weights")
 
 
+def test_large_scores_mix_both_passes(dev):
+    """Scores far above tile 0's row maximum.  Query rows [256, 512) scaled by 8 (their
+    256-row workgroup must take the checked pass, the others the fast one) and key 1400
+    scaled by 3 (the fast pass then runs with a running max below the true maximum);
+    every row against the oracle.  The layer variant scales head 1's w_q by 8: logits
+    that large magnify the unavoidable bf16 rounding of the normalised Q and K that the
+    matrix cores consume (about 2^-9 relative per element), so that variant is checked
+    against the oracle's fp64 prologue rounded to bf16, then the oracle's attention."""
+    from oracle import oracle as O
+    n, s = 1500, 1536
+    w = small(n, s, heads=2, seed=57)
+    inp = W.generate(w, tail="nan")
+    inp["q"][0, 256:512] = (inp["q"][0, 256:512].float() * 8).to(torch.bfloat16)
+    inp["k"][0, 1400] = (inp["k"][0, 1400].float() * 3).to(torch.bfloat16)
+    d = to_dev(inp, dev)
+    say("[edge] large scores, varlen")
+    out = gpu_varlen(w, d)
+    assert_tail_zero(out, [n], "large scores varlen")
+    rows = list(range(n))
+    assert_close(rows_of(out, rows), oracle_varlen(w, inp, rows), "large scores varlen")
+
+    wq = torch.stack([inp["w_q"], inp["w_q"]]).float()
+    wq[1] *= 8
+    wq = wq.to(torch.bfloat16)
+    wk = torch.stack([inp["w_k"], inp["w_k"]])
+    say("[edge] large scores, layer (head 1 w_q x 8)")
+    out = B.attn_layer(d["q"], d["k"], d["v"], wq.to(dev), wk.to(dev), n, w.eps, gpu_rope(w),
+                       scale_of(w))
+    torch.cuda.synchronize()
+    rope = O.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
+
+    def normed_bf16(x, wt):  # [S, H, D] bf16 bits: oracle prologue, rounded to bf16
+        y = O.prologue(W.bits(x), n, W.bits(wt), w.eps, rope, np.arange(n), w_head_stride=128)
+        full = torch.zeros((s, 2, 128), dtype=torch.bfloat16)
+        full[:n] = torch.from_numpy(y).to(torch.float32).to(torch.bfloat16)
+        return full
+
+    ref = O.attn_varlen(W.bits(normed_bf16(inp["q"][0], wq)),
+                        W.bits(normed_bf16(inp["k"][0], wk)), W.bits(inp["v"][0]), n,
+                        scale_of(w), np.asarray(rows))
+    assert_close(rows_of(out, rows), ref, "large scores layer")
+
+
 def test_equal_keys_give_mean_of_values_at_full_length(dev):
     """All valid K rows zero: every score is 0 after RMSNorm + RoPE, so each output row is
     the mean of the valid V rows (any Q) - a property that holds at any size."""
