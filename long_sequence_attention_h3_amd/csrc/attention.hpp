@@ -17,18 +17,19 @@
 //       -- stage tile j+2 into LDS; barrier; load tile j+3 --
 //
 // QK: S^T = K Q^T (two 32-key halves); M: row max of the new scores, raising the running
-// max where it is exceeded (rare branch); E: p = exp2(c s); C: p -> bf16 and row sums;
+// max where it is exceeded (rare branch); E: p = exp2(c (s - m)); C: p -> bf16 and
+// row sums;
 // PV: O^T += V^T P^T.  The scores of tiles j and j+1 live in two register sets used
 // alternately (loop unrolled by two).
 //
-// Arithmetic.  Scores s = q.k are exact bf16 products summed in fp32, in raw units; the
-// QK accumulation starts from -m (the running max) as its C operand, so the accumulator
-// holds s - m and p = exp2(c (s - m)) with c = softmax_scale * log2(e) applied in fp32
-// (pre-scaling Q by c in bf16 would save the multiply but add a score error growing with
-// the logits).  The running max is raised only when a score exceeds it by more than
-// kTauP / c, so p <= 2^8 and the O rescale is rare.  Keys >= N in the last tile start
-// from -inf instead.  Row sums use v_dot2_f32_bf16 on the bf16-rounded p, so the
-// normaliser matches the weights fed to the PV product exactly.
+// Arithmetic.  Scores s = q.k are exact bf16 products summed in fp32 (the QK
+// accumulation starts from the inline constant 0), and p = exp2(fma(s, c, -m c)) with
+// c = softmax_scale * log2(e) applied in fp32: one FMA and one exp2 per score.
+// (Pre-scaling Q by c in bf16 would save nothing here and add a score error growing
+// with the logits.)  The running max m is raised only when a score exceeds it by more
+// than kTauP / c, so p <= 2^8 and the O rescale is rare.  Keys >= N of the last tile get
+// -inf scores.  Row sums use v_dot2_f32_bf16 on the bf16-rounded p, so the normaliser
+// matches the weights fed to the PV product exactly.
 //
 // Memory.  Eight waves (256 query rows) share each K/V tile.  Tiles (prepared by
 // kv_pack_kernel as padded 35 KiB images, layout in common.hpp) go through a 3-slot LDS
@@ -82,23 +83,24 @@ struct Wave {
   bf16x8 q[8];      // Q^T B operands
   f32x16 o[4];      // O^T accumulators per 32-channel block
   bf16x8 p[4];      // P^T B operands per 16-key step
-  f32x16 negm;      // C operand of QK: -m, splat
-  float m, l;       // running max (raw score units), row-sum partial over this lane's keys
+  float m;          // running max (raw score units)
+  float nmc;        // -m * c, the exp2 offset
+  float mt;         // m + kTauP / c: scores above it raise the running max
+  float l;          // row-sum partial over this lane's keys
   float c;          // softmax_scale * log2(e)
   float tau;        // kTauP / c: the running-max slack in raw units
 };
 
 // S^T (64 keys x 32 rows, as two 32-key halves).  `kb_base` = this lane's K operand
 // address in the slot: key row l32, channel chunk hl; the (kb, ks) operand sits at
-// + kb*32 rows + ks*32 bytes.  The accumulation starts from c0[kb].
-__device__ __forceinline__ void qk(const Wave& w, f32x16* s, const char* kb_base,
-                                   const f32x16* c0) {
+// + kb*32 rows + ks*32 bytes.
+__device__ __forceinline__ void qk(const Wave& w, f32x16* s, const char* kb_base) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_base + kb * 32 * kKRowPitch + ks * 32);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.q[ks], ks == 0 ? c0[kb] : s[kb], 0,
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.q[ks], ks == 0 ? f32x16{} : s[kb], 0,
                                                       0, 0);
     }
   }
@@ -117,12 +119,33 @@ __device__ __forceinline__ void pv(Wave& w, const char* vb_base) {
   }
 }
 
-// E: p = exp2(c acc), in place.
+// E: p = exp2(c (s - m)), in place.
+__device__ __forceinline__ float ex1(const Wave& w, float s) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(s, w.c, w.nmc));
+}
 __device__ __forceinline__ void ex(const Wave& w, f32x16* s) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[kb][e] = __builtin_amdgcn_exp2f(s[kb][e] * w.c);
+    for (int e = 0; e < 16; ++e) s[kb][e] = ex1(w, s[kb][e]);
+}
+
+// Set the running max to v where `need` (wave-uniform call); with kRescale, scale O and
+// l by exp2(c (m_old - m_new)) for those rows.
+template <bool kRescale>
+__device__ __forceinline__ void raise_max(Wave& w, bool need, float v) {
+  const float m_new = need ? v : w.m;
+  if (kRescale) {
+    const float alpha = __builtin_amdgcn_exp2f((w.m - m_new) * w.c);
+    w.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) w.o[db][e] *= alpha;
+  }
+  w.m = m_new;
+  w.nmc = -m_new * w.c;
+  w.mt = m_new + w.tau;
 }
 
 // C: p -> bf16 operands; row sum of the rounded values (v_dot2_f32_bf16 with (1, 1)).
@@ -148,35 +171,14 @@ __device__ __forceinline__ void cv(Wave& w, const f32x16* s) {
   w.l = acc0 + acc1;
 }
 
-// M: tile row max of acc; raise the running max where it is exceeded by more than
-// kTauP / c (always on the first tile).  Rare path: rescale O and l, shift acc and -m.
-template <bool kFirst>
-__device__ __forceinline__ void mx(Wave& w, f32x16* s) {
+// M on the first tile: the running max starts at the tile's row max.
+__device__ __forceinline__ void mx_first(Wave& w, const f32x16* s) {
   float v = s[0][0];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) v = fmaxf(v, s[kb][e]);
-  v = pair_max(v);
-  const bool need = kFirst || v > w.tau;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float delta = need ? v : 0.0f;
-    w.m += delta;
-    if (!kFirst) {
-      const float alpha = __builtin_amdgcn_exp2f(-delta * w.c);
-      w.l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) w.o[db][e] *= alpha;
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) w.negm[e] = -w.m;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] -= delta;
-  }
+  raise_max<false>(w, true, pair_max(v));
 }
 
 // One steady-state step as an explicit instruction order.  kCheck: also take the row
@@ -192,7 +194,7 @@ __device__ __forceinline__ void mx(Wave& w, f32x16* s) {
 template <bool kCheck>
 __device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
                                             const char* kbase, const char* vbase,
-                                            const f32x16* c0, float& vmax) {
+                                            float& vmax) {
   bf16x8 kop[16], vop[16];
   auto read_k = [&](int i) {  // operand of QK MFMA i: kb = i & 1, ks = i >> 1
     kop[i] = *reinterpret_cast<const bf16x8*>(kbase + (i & 1) * 32 * kKRowPitch +
@@ -241,13 +243,11 @@ __device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
 #pragma unroll
   for (int i = 0; i < 16; ++i) {  // QK(j+1) || exp(j), convert/sum(j)
     const int kb = i & 1, ks = i >> 1;
-    nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], w.q[ks], ks == 0 ? c0[kb] : nxt[kb],
+    nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], w.q[ks], ks == 0 ? f32x16{} : nxt[kb],
                                                       0, 0, 0);
     read(i + 3);
-    cur[(2 * i) >> 4][(2 * i) & 15] =
-        __builtin_amdgcn_exp2f(cur[(2 * i) >> 4][(2 * i) & 15] * w.c);
-    cur[(2 * i + 1) >> 4][(2 * i + 1) & 15] =
-        __builtin_amdgcn_exp2f(cur[(2 * i + 1) >> 4][(2 * i + 1) & 15] * w.c);
+    cur[(2 * i) >> 4][(2 * i) & 15] = ex1(w, cur[(2 * i) >> 4][(2 * i) & 15]);
+    cur[(2 * i + 1) >> 4][(2 * i + 1) & 15] = ex1(w, cur[(2 * i + 1) >> 4][(2 * i + 1) & 15]);
     if (i >= 4) {
       cv_op((i - 4) >> 2, 2 * ((i - 4) & 3));
       cv_op((i - 4) >> 2, 2 * ((i - 4) & 3) + 1);
@@ -274,26 +274,12 @@ __device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
   vmax = v;
 }
 
-// Rest of M after steady_step: row max across the lane pair, raise where needed.
-__device__ __forceinline__ void mx_finish(Wave& w, f32x16* s, float v) {
+// Rest of M after steady_step: row max across the lane pair; raise the running max
+// where it is exceeded by more than kTauP / c (rare branch).
+__device__ __forceinline__ void mx_finish(Wave& w, float v) {
   v = pair_max(v);
-  const bool need = v > w.tau;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float delta = need ? v : 0.0f;
-    w.m += delta;
-    const float alpha = __builtin_amdgcn_exp2f(-delta * w.c);
-    w.l *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) w.o[db][e] *= alpha;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) w.negm[e] = -w.m;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] -= delta;
-  }
+  const bool need = v > w.mt;
+  if (__builtin_amdgcn_ballot_w64(need)) raise_max<true>(w, need, v);
 }
 
 }  // namespace attn
@@ -387,9 +373,9 @@ attn_fwd_kernel(AttnArgs a) {
   w.c = c2;
   w.tau = kTauP / c2;
   w.m = 0.0f;
+  w.nmc = 0.0f;
+  w.mt = 0.0f;
   w.l = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) w.negm[e] = 0.0f;
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
 
@@ -420,28 +406,24 @@ attn_fwd_kernel(AttnArgs a) {
   const int k_lane = l32 * kKRowPitch + hl * 16;
   const int v_lane = kKImageBytes + l32 * kVRowPitch + hl * 16;
 
-  // QK of tile t into s.  kMask (the last tile): the C operand is -inf for keys >= tail;
-  // register 4i+j of half kb holds key kb*32 + 8i + 4hl + j.  Decided at compile time so
-  // that no branch separates the products from the work they overlap.
-  auto qk_tile = [&](f32x16* s, int t, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool kMask = decltype(mask_tag)::value;
-    f32x16 c[2] = {w.negm, w.negm};
-    if (kMask) {
+  // Keys >= tail of the last tile get -inf scores (so p = 0); register 4i+j of half kb
+  // holds key kb*32 + 8i + 4hl + j.  Applied after the product, once per workgroup.
+  auto mask_tail = [&](f32x16* s) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = kb * 32 + 8 * i + 4 * hl + j;
-            if (key >= tail) c[kb][4 * i + j] = -INFINITY;
-          }
-    }
-    qk(w, s, slot(t) + k_lane, c);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int key = kb * 32 + 8 * i + 4 * hl + jj;
+          s[kb][4 * i + jj] = key >= tail ? -INFINITY : s[kb][4 * i + jj];
+        }
   };
 
   // One pipeline step for tile j: `cur` holds acc of tile j (max already applied), `nxt`
-  // receives tile j+1.  kNext: tile j+1 exists; kMaskNext: it is the last tile.
+  // receives tile j+1.  kNext: tile j+1 exists; kMask: it is the last tile.  The
+  // choices are compile-time so that no branch separates the products from the work
+  // they overlap.
   auto step = [&](f32x16* cur, f32x16* nxt, int j, auto next_tag, auto mask_tag,
                   auto check_tag) __attribute__((always_inline)) {
     constexpr bool kNext = decltype(next_tag)::value;
@@ -449,21 +431,19 @@ attn_fwd_kernel(AttnArgs a) {
     constexpr bool kChk = decltype(check_tag)::value;
     if (j + kSlots - 1 < nt) load(j + kSlots - 1);  // into the slot tile j-1 left
     if (kNext) {
-      f32x16 c[2] = {w.negm, w.negm};
-      if (kMask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int key = kb * 32 + 8 * i + 4 * hl + jj;
-              if (key >= tail) c[kb][4 * i + jj] = -INFINITY;
-            }
-      }
       float v;
-      steady_step<kChk>(w, cur, nxt, slot(j + 1) + k_lane, slot(j) + v_lane, c, v);
-      if (kChk) mx_finish(w, nxt, v);
+      steady_step<kChk>(w, cur, nxt, slot(j + 1) + k_lane, slot(j) + v_lane, v);
+      if (kMask) {
+        mask_tail(nxt);
+        if (kChk) {  // the max taken in the step saw the masked keys: take it again
+          v = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v = fmaxf(v, nxt[kb][e]);
+        }
+      }
+      if (kChk) mx_finish(w, v);
     } else {  // last tile: no next scores
       ex(w, cur);
       cv(w, cur);
@@ -482,11 +462,9 @@ attn_fwd_kernel(AttnArgs a) {
   loads_done();
   __syncthreads();
   f32x16 sa[2], sb[2];
-  if (nt == 1)
-    qk_tile(sa, 0, T{});
-  else
-    qk_tile(sa, 0, F{});
-  mx<true>(w, sa);  // the running max starts at tile 0's row max
+  qk(w, sa, slot(0) + k_lane);
+  if (nt == 1) mask_tail(sa);
+  mx_first(w, sa);  // the running max starts at tile 0's row max
 
   // Score bound.  Every score of this lane's row satisfies s <= |q| * max_j |k_j|
   // (Cauchy-Schwarz), and the running max starts at tile 0's row maximum m0, a lower
@@ -519,24 +497,28 @@ attn_fwd_kernel(AttnArgs a) {
     if (fail) return;
   }
 
-  // steady steps: tile j+1 exists and is not the last (j <= nt-3), two at a time
+  // Steps.  Step j (tile j current, tile j+1 next) for j < nt-2 is a steady step; then
+  // come step nt-2 (its next tile is the last, masked) and step nt-1 (no next tile).
+  // The score sets alternate sa -> sb -> sa; for every path to reach the loop with the
+  // current tile in sa and leave it with the same, an odd count of steady steps peels
+  // one first.
   using Check = std::integral_constant<bool, kCheck>;
-  int j = 0;
-  for (; j + 4 <= nt; j += 2) {
-    step(sa, sb, j, T{}, F{}, Check{});
-    step(sb, sa, j + 1, T{}, F{}, Check{});
-  }
-  // the last one to three steps; `sa` holds the current tile here
-  const int r = nt - j;
-  if (r == 3) {
-    step(sa, sb, j, T{}, F{}, Check{});
-    step(sb, sa, j + 1, T{}, T{}, Check{});
-    step(sa, sb, j + 2, F{}, F{}, Check{});
-  } else if (r == 2) {
-    step(sa, sb, j, T{}, T{}, Check{});
-    step(sb, sa, j + 1, F{}, F{}, Check{});
+  if (nt == 1) {
+    step(sa, sb, 0, F{}, F{}, Check{});
   } else {
-    step(sa, sb, j, F{}, F{}, Check{});
+    int j = 0;
+    if (nt & 1) {
+      step(sa, sb, 0, T{}, F{}, Check{});
+      sa[0] = sb[0];
+      sa[1] = sb[1];
+      j = 1;
+    }
+    for (; j < nt - 2; j += 2) {
+      step(sa, sb, j, T{}, F{}, Check{});
+      step(sb, sa, j + 1, T{}, F{}, Check{});
+    }
+    step(sa, sb, nt - 2, T{}, T{}, Check{});
+    step(sb, sa, nt - 1, F{}, F{}, Check{});
   }
 
   // ---- epilogue: lane holds O[row][d = db*32 + 8i + 4hl + j] at register 4i+j
