@@ -11,6 +11,9 @@ inputs already resident in HBM.  Prints one JSON line:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload
              (sampled query rows of every head), whose rows also gate parity
   kernels    the other kernels' achieved bandwidth (K/V pre-pass, standalone prologue)
+  per_workload  every workload size: h3_attn_layer and h3_attn_varlen TFLOP/s (median and
+             min of 10 calls after 3 warm-up calls) and h3_qk_rmsnorm_rope GB/s
+  sclk_mhz   the shader clock the driver reported right after the timed region
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
        python bench.py --only attn   (K/V pre-pass once, then K attention launches only:
@@ -78,6 +81,78 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def sclk_mhz():
+    """Current shader clock from the driver's DPM table (the level marked '*'), or None."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        return int("".join(ch for ch in line.split(":", 1)[1] if ch.isdigit()))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def call_times(torch, stream, fn, warmup: int = 3, reps: int = 10):
+    """Per-call HIP-event times (ms) of `fn` on `stream` after `warmup` untimed calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+
+def per_workload(torch, B, W, dev, stream):
+    """h3_attn_layer / h3_attn_varlen TFLOP/s and prologue GB/s on every workload size."""
+    import statistics
+    table = {}
+    for idx, w in sorted(W.WORKLOADS.items()):
+        inp = W.generate(w, tail="nan")
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        del inp
+        rope = B.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
+        scale = 1.0 / math.sqrt(w.head_dim)
+        n = d["n_valid"]
+        out = torch.empty_like(d["q"])
+        ws = torch.empty(B.workspace_size(d["q"]), dtype=torch.uint8, device=dev)
+        q2, k2 = torch.empty_like(d["q"]), torch.empty_like(d["k"])
+        row = {"heads": w.heads, "n_valid": w.n_valid, "seq_buf": w.seq_buf,
+               "flop": w.flops}
+        calls = {
+            "h3_attn_layer": lambda: B.attn_layer(d["q"], d["k"], d["v"], d["w_q"], d["w_k"], n,
+                                                  w.eps, rope, scale, out=out, workspace=ws),
+            "h3_attn_varlen": lambda: B.attn_varlen(d["q"], d["k"], d["v"], n, scale, out=out,
+                                                    workspace=ws),
+        }
+        for name, fn in calls.items():
+            t = call_times(torch, stream, fn)
+            med, mn = statistics.median(t), min(t)
+            row[name] = {"ms_median": round(med, 4), "ms_min": round(mn, 4),
+                         "tflops_median": round(w.flops / med / 1e9, 2),
+                         "tflops_best": round(w.flops / mn / 1e9, 2),
+                         "frac_bf16_peak_median": round(w.flops / med / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        t = call_times(torch, stream, lambda: B.qk_rmsnorm_rope(
+            d["q"], d["k"], d["w_q"], d["w_k"], n, w.eps, rope, q_out=q2, k_out=k2))
+        med = statistics.median(t)
+        nbytes = 2 * 2 * w.batch * w.n_valid * w.heads * w.head_dim * 2
+        row["h3_qk_rmsnorm_rope"] = {"ms_median": round(med, 4), "bytes": nbytes,
+                                     "GB/s": round(nbytes / med / 1e6, 1)}
+        table[w.name] = row
+        log(f"[bench] {w.name}: layer {row['h3_attn_layer']['tflops_median']} TFLOP/s, varlen "
+            f"{row['h3_attn_varlen']['tflops_median']} TFLOP/s, prologue "
+            f"{row['h3_qk_rmsnorm_rope']['GB/s']} GB/s")
+        del d, out, ws, q2, k2
+        torch.cuda.empty_cache()
+    return table
+
+
 def copy_only(torch, dev, steps: int) -> int:
     """A plain device-to-device copy of 2 GiB, `steps` times: 2 GiB read and 2 GiB
     written per launch, the known sizes the traffic counters are scaled by."""
@@ -96,7 +171,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--cpu-rows-per-head", type=int, default=2048)
+    ap.add_argument("--cpu-rows-per-head", type=int, default=4096)
+    ap.add_argument("--no-per-workload", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=("all", "attn", "copy"), default="all")
     args = ap.parse_args()
@@ -157,6 +233,7 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
+    sclk = sclk_mhz()
     flops = w.flops
     value = flops / (ms_step * 1e-3) / 1e12
     log(f"[bench] h3_attn_layer {ms_step:.3f} ms/step  {value:.1f} TFLOP/s "
@@ -239,6 +316,7 @@ def main() -> int:
                                                       PEAK_HBM_GBS, 4)},
         },
         "wall_s_timed_region": round(wall, 4),
+        "sclk_mhz": sclk,
         "source_hash": source_hash(),
     }
 
@@ -277,6 +355,10 @@ def main() -> int:
             print(json.dumps(result), flush=True)
             log("[bench] parity FAILED against the oracle")
             return 1
+    if not args.no_per_workload:
+        del d, out, ws, q2, k2, layer_out
+        torch.cuda.empty_cache()
+        result["per_workload"] = per_workload(torch, B, W, dev, stream)
     print(json.dumps(result), flush=True)
     return 0
 
