@@ -6,38 +6,46 @@
 // sequence length and the structural tail padding is not computed; §3.2: the Q/K
 // RMSNorm + RoPE prologue is fused (the Q half here, in registers).
 //
-// Why the pipeline.  On gfx950 a wave can issue VALU work while its own MFMA runs, but
-// only a few instructions' worth per MFMA (about two v_exp_f32 or four full-rate ops per
-// 32x32x16 MFMA are hidden); VALU work of another wave on the same SIMD overlaps much
-// less.  So each wave interleaves the softmax of one 64-key tile with the matrix
-// products of its neighbours.  Per tile j, for the wave's 32 query rows:
+// Where the time goes (measured on gfx950).  With 32 query rows per wave, every
+// 32x32x16 MFMA consumes one 1 KiB operand read from LDS; at the full MFMA rate a CU
+// would need about as many LDS bytes per cycle as the LDS delivers, and these reads,
+// with the tile copies into LDS, are the main limit.  VALU work of the softmax overlaps
+// the MFMAs only in part (per MFMA, one exp2 costs a few percent of MFMA throughput).
+// Holding 64 rows per wave halves the LDS reads per MFMA but needs one wave per SIMD,
+// which leaves every barrier and memory wait unhidden; it measured slower.  Spreading
+// the softmax work evenly over all 32 MFMA slots of a step, or summing the rows with
+// plain adds instead of v_dot2_f32_bf16, measured no faster either.
 //
-//   B1: QK(j+1)  MFMA x16  ||  E(j)          (32 multiply + exp2)
-//   B2: PV(j)    MFMA x16  ||  C(j), M(j+1)   (bf16 convert + row sums, row max + check)
-//       -- stage tile j+2 into LDS; barrier; load tile j+3 --
+// The pipeline.  Two waves per SIMD; each wave interleaves the softmax of one 64-key
+// tile with the matrix products of its neighbours.  Per tile j, for its 32 query rows:
+//
+//   B1: QK(j+1)  MFMA x16  ||  E(j), C(j) of the first groups   (fma + exp2, convert)
+//   B2: PV(j)    MFMA x16  ||  C(j) of the last group, M(j+1) if checked
+//       -- tile j+2 lands in LDS; barrier; the copy of tile j+3 starts --
 //
 // QK: S^T = K Q^T (two 32-key halves); M: row max of the new scores, raising the running
-// max where it is exceeded (rare branch); E: p = exp2(c (s - m)); C: p -> bf16 and
-// row sums;
-// PV: O^T += V^T P^T.  The scores of tiles j and j+1 live in two register sets used
-// alternately (loop unrolled by two).
+// max where it is exceeded (rare branch); E: p = exp2(c (s - m)); C: p -> bf16 operands
+// and row sums; PV: O^T += V^T P^T.  The scores of tiles j and j+1 live in two register
+// sets used alternately (loop unrolled by two).
 //
 // Arithmetic.  Scores s = q.k are exact bf16 products summed in fp32 (the QK
 // accumulation starts from the inline constant 0), and p = exp2(fma(s, c, -m c)) with
 // c = softmax_scale * log2(e) applied in fp32: one FMA and one exp2 per score.
-// (Pre-scaling Q by c in bf16 would save nothing here and add a score error growing
-// with the logits.)  The running max m is raised only when a score exceeds it by more
-// than kTauP / c, so p <= 2^8 and the O rescale is rare.  Keys >= N of the last tile get
-// -inf scores.  Row sums use v_dot2_f32_bf16 on the bf16-rounded p, so the normaliser
-// matches the weights fed to the PV product exactly.
+// (Pre-scaling Q by c in bf16 would save the FMA but add a score error growing with
+// the logits.)  The running max m is raised only when a score exceeds it by more than
+// kTauP / c, so p <= 2^8 and the O rescale is rare.  Keys >= N of the last tile get
+// -inf scores.  P is rounded to bf16 for the PV product, and the row sums add exactly
+// those rounded values (v_dot2_f32_bf16 with (1, 1)), so every output row is a true
+// weighted average of V rows; summing the unrounded fp32 p instead costs up to 2^-9
+// relative error on strongly peaked rows.
 //
 // Memory.  Eight waves (256 query rows) share each K/V tile.  Tiles (prepared by
 // kv_pack_kernel as padded 35 KiB images, layout in common.hpp) go through a 3-slot LDS
-// ring: tile j is read from B1(j-1) to B2(j).  Tile j+2 is copied global -> LDS directly
-// (global_load_lds_dwordx4, no staging registers) during step j into the slot tile j-1
-// left, and waited for at the step's end, before its one barrier.  Every operand read is
-// one base register plus an immediate offset.  Everything fits in 256 VGPRs per lane, two
-// waves per SIMD.
+// ring: tile j is read from step j-1 (QK) to step j (PV).  Tile j+2 is copied
+// global -> LDS directly (global_load_lds_dwordx4, no staging registers) during step j
+// into the slot tile j-1 left, and waited for at the step's end, before its one
+// barrier.  Every operand read is one base register plus an immediate offset.
+// Everything fits in 256 VGPRs per lane, two waves per SIMD.
 #pragma once
 
 #include <type_traits>
@@ -69,10 +77,7 @@ constexpr float kTauP = 8.0f;  // log2 units
 
 namespace attn {
 
-#ifndef H3_ATTN_SLOTS
-#define H3_ATTN_SLOTS 3
-#endif
-constexpr int kSlots = H3_ATTN_SLOTS;       // LDS ring depth (tiles)
+constexpr int kSlots = 3;                    // LDS ring depth (tiles)
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;           // query rows per workgroup
@@ -284,6 +289,91 @@ __device__ __forceinline__ void mx_finish(Wave& w, float v) {
 
 }  // namespace attn
 
+// The 8 Q^T B operands of one query row (lane: channels 16ks + 8hl .. +8), as bf16;
+// zeros for rows >= N.  With kFusedQ the row is RMS-normalised and rotated on the way,
+// with the same helpers, operation order and pairwise-tree RMS sum as
+// qk_norm_rope_kernel, so the values are the ones h3_qk_rmsnorm_rope writes.  All 64
+// lanes must be active (lane pairs l, l^32 share the row).
+template <bool kFusedQ>
+__device__ __forceinline__ void load_q_operands(const AttnArgs& a, int64_t row, int head, int hl,
+                                                const FreqTable* ft, bf16x8* q) {
+  const bool row_valid = row < a.n_valid;
+  const __bf16* qrow = a.q + row * a.in_stride + (int64_t)head * kHeadDim;
+  u32x4 raw[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    raw[ks] = row_valid ? *reinterpret_cast<const u32x4*>(qrow + (2 * ks + hl) * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
+  if (kFusedQ) {
+    // RMS of the row: partials of the 8 own chunks, the other 8 from lane l^32, combined
+    // in the canonical pairwise tree (chunks c, c^1, then c^2, c^4, c^8).
+    float part[8], other[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      float x[8];
+      unpack8(raw[ks], x);
+      part[ks] = chunk_sumsq(x);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) other[ks] = other_half(part[ks]);
+    float s1[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) s1[ks] = hl ? other[ks] + part[ks] : part[ks] + other[ks];
+    const float s2[4] = {s1[0] + s1[1], s1[2] + s1[3], s1[4] + s1[5], s1[6] + s1[7]};
+    const float s3[2] = {s2[0] + s2[1], s2[2] + s2[3]};
+    const float inv = inv_rms(s3[0] + s3[1], a.eps);
+    const __bf16* wq = a.w_q + (int64_t)head * a.w_head_stride;
+#pragma unroll 1
+    for (int ks = 0; ks < 8; ++ks) {
+      const int cc = 2 * ks + hl;
+      const ChunkRot cr = chunk_rotation(a.rope, row, cc);
+      float x[8], xp[8], wv[8], wpv[8], y[8];
+      unpack8(raw[ks], x);
+      const u32x4 praw = row_valid ? *reinterpret_cast<const u32x4*>(qrow + cr.partner * 8)
+                                   : u32x4{0u, 0u, 0u, 0u};
+      unpack8(praw, xp);
+      unpack8(*reinterpret_cast<const u32x4*>(wq + cc * 8), wv);
+      unpack8(*reinterpret_cast<const u32x4*>(wq + cr.partner * 8), wpv);
+      norm_rotate_chunk(x, xp, wv, wpv, inv, cr, ft, y);
+      raw[ks] = pack8(y);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) q[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+}
+
+// Workgroups whose rows all lie in [N, S): write zeros (the caller returns after).
+__device__ __forceinline__ void zero_rows(const AttnArgs& a, int64_t m0, int rows_per_wg,
+                                          int head, int tid, int nthreads) {
+  const int64_t rows = (a.seq_buf - m0) < rows_per_wg ? (a.seq_buf - m0) : rows_per_wg;
+  const int64_t hoff = (int64_t)head * kHeadDim;
+  for (int64_t i = tid; i < rows * kChunks; i += nthreads) {
+    const int64_t r = m0 + i / kChunks;
+    *reinterpret_cast<u32x4*>(a.o + r * a.out_stride + hoff + (i % kChunks) * 8) =
+        u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Largest K row norm over the head's nt tiles (from the tile images' pads), every lane.
+__device__ __forceinline__ float head_kmax(const char* img, int nt, int lane) {
+  float kmax = 0.0f;
+  for (int t = lane; t < nt; t += 64)
+    kmax = fmaxf(kmax, *reinterpret_cast<const float*>(img + (int64_t)t * kTileImageBytes +
+                                                        kKNormOffset));
+  for (int off = 32; off >= 1; off >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off, 64));
+  return kmax;
+}
+
+// |q|^2 of this lane's row from its 8 B operands (the other half comes from lane l^32).
+__device__ __forceinline__ float q_norm2(const bf16x8* q) {
+  float q2 = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q2 = fmaf((float)q[ks][e], (float)q[ks][e], q2);
+  return pair_sum(q2);
+}
+
 // kCheck = false: the fast pass; workgroups whose scores are not provably bounded are
 // flagged in wg_checked and left alone.  kCheck = true: the second pass; runs the flagged
 // workgroups with the per-tile running-max check and returns at once for the others.
@@ -307,12 +397,7 @@ attn_fwd_kernel(AttnArgs a) {
   if (kCheck && a.wg_checked[wg] == 0) return;  // done by the fast pass
   if (m0 >= a.n_valid) {  // rows past the valid length: zeros only
     if (tid == 0) a.wg_checked[wg] = 0;
-    const int64_t rows = (a.seq_buf - m0) < kRows ? (a.seq_buf - m0) : kRows;
-    for (int64_t i = tid; i < rows * kChunks; i += kThreads) {
-      const int64_t r = m0 + i / kChunks;
-      *reinterpret_cast<u32x4*>(a.o + r * a.out_stride + hoff + (i % kChunks) * 8) =
-          u32x4{0u, 0u, 0u, 0u};
-    }
+    zero_rows(a, m0, kRows, head, tid, kThreads);
     return;
   }
   if (kFusedQ) {
@@ -325,51 +410,7 @@ attn_fwd_kernel(AttnArgs a) {
   const int64_t row = m0 + wave * 32 + l32;
   const bool row_valid = row < a.n_valid;
 
-  // ---- Q row -> B operands (lane: channels 16ks + 8hl .. +8)
-  {
-    const __bf16* qrow = a.q + row * a.in_stride + hoff;
-    u32x4 raw[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      raw[ks] = row_valid ? *reinterpret_cast<const u32x4*>(qrow + (2 * ks + hl) * 8)
-                          : u32x4{0u, 0u, 0u, 0u};
-    if (kFusedQ) {
-      // RMS of the row: partials of the 8 own chunks, the other 8 from lane l^32, combined
-      // in the canonical pairwise tree (chunks c, c^1, then c^2, c^4, c^8).
-      float part[8], other[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        float x[8];
-        unpack8(raw[ks], x);
-        part[ks] = chunk_sumsq(x);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) other[ks] = other_half(part[ks]);
-      float s1[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s1[ks] = hl ? other[ks] + part[ks] : part[ks] + other[ks];
-      const float s2[4] = {s1[0] + s1[1], s1[2] + s1[3], s1[4] + s1[5], s1[6] + s1[7]};
-      const float s3[2] = {s2[0] + s2[1], s2[2] + s2[3]};
-      const float inv = inv_rms(s3[0] + s3[1], a.eps);
-      const __bf16* wq = a.w_q + (int64_t)head * a.w_head_stride;
-#pragma unroll 1
-      for (int ks = 0; ks < 8; ++ks) {
-        const int cc = 2 * ks + hl;
-        const ChunkRot cr = chunk_rotation(a.rope, row, cc);
-        float x[8], xp[8], wv[8], wpv[8], y[8];
-        unpack8(raw[ks], x);
-        const u32x4 praw = row_valid ? *reinterpret_cast<const u32x4*>(qrow + cr.partner * 8)
-                                     : u32x4{0u, 0u, 0u, 0u};
-        unpack8(praw, xp);
-        unpack8(*reinterpret_cast<const u32x4*>(wq + cc * 8), wv);
-        unpack8(*reinterpret_cast<const u32x4*>(wq + cr.partner * 8), wpv);
-        norm_rotate_chunk(x, xp, wv, wpv, inv, cr, &ft, y);
-        raw[ks] = pack8(y);  // the same bf16 values h3_qk_rmsnorm_rope writes
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) w.q[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
-  }
+  load_q_operands<kFusedQ>(a, row, head, hl, &ft, w.q);
   w.c = c2;
   w.tau = kTauP / c2;
   w.m = 0.0f;
@@ -394,13 +435,13 @@ attn_fwd_kernel(AttnArgs a) {
     for (int i = 0; i < (kImageChunks + kWaves - 1) / kWaves; ++i) {
       const int c = wave + i * kWaves;
       if (c < kImageChunks)
-        __builtin_amdgcn_global_load_lds(
-            src + c * 1024 + lane * 16, (__attribute__((address_space(3))) void*)(dst + c * 1024),
-            16, 0, 0);
+        dma_to_lds16(src + c * 1024 + lane * 16,
+                     (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(dst + c * 1024));
     }
   };
   // All of this thread's tile loads have landed in LDS (s_waitcnt vmcnt(0)).
   auto loads_done = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };
+
 
   // per-lane operand offsets within a slot (see qk / pv)
   const int k_lane = l32 * kKRowPitch + hl * 16;
@@ -449,7 +490,7 @@ attn_fwd_kernel(AttnArgs a) {
       cv(w, cur);
       pv(w, slot(j) + v_lane);
     }
-    loads_done();  // tile j+1 (and j+2) in LDS before the next step
+    loads_done();  // tile j+2 in LDS before the next step
     __syncthreads();
   };
   using T = std::true_type;
@@ -475,17 +516,8 @@ attn_fwd_kernel(AttnArgs a) {
   // exact running max.  Then the fast pass runs without the per-tile max and its branch;
   // otherwise the workgroup is left to the checked pass.
   if (!kCheck) {
-    float kmax = 0.0f;
-    for (int t = lane; t < nt; t += 64)
-      kmax = fmaxf(kmax, *reinterpret_cast<const float*>(img + (int64_t)t * kTileImageBytes +
-                                                          kKNormOffset));
-    for (int off = 32; off >= 1; off >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, off, 64));
-    float q2 = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q2 = fmaf((float)w.q[ks][e], (float)w.q[ks][e], q2);
-    const float bound = sqrtf(pair_sum(q2)) * 1.0001f * kmax;
+    const float kmax = head_kmax(img, nt, lane);
+    const float bound = sqrtf(q_norm2(w.q)) * 1.0001f * kmax;
     const bool ok = (bound - w.m) * c2 <= 64.0f;  // false for NaN as well
     __shared__ int wave_fail[kWaves];
     if (lane == 0) wave_fail[wave] = __builtin_amdgcn_ballot_w64(!ok) != 0;

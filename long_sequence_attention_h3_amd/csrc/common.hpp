@@ -86,6 +86,26 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Copy 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's 16 bytes at `src` (its own address) land at LDS byte lds_base + 16 i.
+// Issued as inline assembly on purpose: the compiler cannot tell which LDS bytes the
+// copy writes, and for the intrinsic it conservatively waits for every outstanding copy
+// before the next LDS read; the callers instead wait for their own copies explicitly
+// (s_waitcnt vmcnt) and publish them with a barrier before any lane reads the bytes.
+// M0 is a reserved register to the compiler, which ignores it in a clobber list; no
+// other code in this library uses M0, so setting it here disturbs nothing.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_to_lds16(const void* src, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Workgroup -> logical tile.  Consecutive workgroup ids are dispatched round-robin over
 // the 8 XCDs; this bijection hands each XCD one contiguous range of logical tiles, so
 // the workgroups resident on one XCD (sharing its L2) work on the same head.
