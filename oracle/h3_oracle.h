@@ -110,6 +110,33 @@ int h3o_attn_layer(const uint16_t* q, const uint16_t* k, const uint16_t* v, int6
                    double eps, const h3o_rope* rope, double scale, const int64_t* rows,
                    int64_t n_rows, int threads, double* out);
 
+/* ---- FP8 ("SAGE") variant: see h3_oracle_fp8.cpp for the method and its readings. */
+
+/* Nearest FP8 E4M3 value (OCP "fn": bias 7, max 448, subnormals), ties to even,
+ * saturating at +-448.  NaN stays NaN. */
+double h3o_e4m3(double x);
+
+/* Nearest bf16 of x (ties to even), as bits. */
+uint16_t h3o_round_bf16(double x);
+
+/* Quantize n fp32 values with one scale amax/448, in fp32 like the kernel: codes[i] =
+ * E4M3(clamp(x[i] * (448 / amax))) as values; *scale = amax / 448 (0 if all zero). */
+void h3o_quantize_group(const float* x, int64_t n, double* codes, double* scale);
+
+/* FP8 attention on bf16 buffers whose Q and K are already normalised and rotated
+ * (same layouts and row semantics as h3o_attn_varlen). */
+int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        int64_t seq_buf, int64_t n_valid, int64_t heads, int64_t d,
+                        int64_t row_stride, double scale, const int64_t* rows, int64_t n_rows,
+                        int threads, double* out);
+
+/* The FP8 layer: prologue of Q and K (fp64, rounded to bf16), then h3o_attn_varlen_fp8. */
+int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_buf,
+                       int64_t n_valid, int64_t heads, int64_t d, int64_t row_stride,
+                       const uint16_t* w_q, const uint16_t* w_k, int64_t w_head_stride,
+                       double eps, const h3o_rope* rope, double scale, const int64_t* rows,
+                       int64_t n_rows, int threads, double* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,4 +1,4 @@
-"""ctypes wrapper of the fp64 CPU oracle (``h3_oracle.cpp``).
+"""ctypes wrapper of the fp64 CPU oracle (``h3_oracle.cpp``, ``h3_oracle_fp8.cpp``).
 
 TEST INFRASTRUCTURE ONLY.  Importable by the tests, the smoke check and the
 benchmark's CPU-baseline leg; the product package never imports it.
@@ -16,19 +16,20 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "h3_oracle.cpp")
+_SRCS = [os.path.join(_HERE, "h3_oracle.cpp"), os.path.join(_HERE, "h3_oracle_fp8.cpp")]
 _LIB = os.path.join(_HERE, "libh3oracle.so")
 
 # Plain -O3 (vectorises the independent per-key / per-channel loops); no
 # -ffast-math and no FMA contraction, so each product and sum is rounded as written.
 GXX_CMD = ["g++", "-O3", "-std=c++17", "-fPIC", "-shared", "-pthread",
-           "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", _LIB]
+           "-ffp-contract=off", "-fno-fast-math", *_SRCS, "-o", _LIB]
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle shared library (idempotent unless ``force``)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
-            os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "h3_oracle.h"))):
+            [os.path.getmtime(f) for f in _SRCS] +
+            [os.path.getmtime(os.path.join(_HERE, "h3_oracle.h"))]):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = GXX_CMD[:-1] + [tmp]
         subprocess.run(cmd, check=True)
@@ -84,6 +85,18 @@ def lib():
         _lib.h3o_attn_layer.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, I64, D,
                                         ctypes.POINTER(Rope), D, P, I64, I, P]
         _lib.h3o_attn_layer.restype = I
+        _lib.h3o_e4m3.argtypes = [D]
+        _lib.h3o_e4m3.restype = D
+        _lib.h3o_round_bf16.argtypes = [D]
+        _lib.h3o_round_bf16.restype = ctypes.c_uint16
+        _lib.h3o_quantize_group.argtypes = [P, I64, P, P]
+        _lib.h3o_quantize_group.restype = None
+        _lib.h3o_attn_varlen_fp8.argtypes = [P, P, P, I64, I64, I64, I64, I64, D, P, I64,
+                                             I, P]
+        _lib.h3o_attn_varlen_fp8.restype = I
+        _lib.h3o_attn_layer_fp8.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, I64, D,
+                                            ctypes.POINTER(Rope), D, P, I64, I, P]
+        _lib.h3o_attn_layer_fp8.restype = I
     return _lib
 
 
@@ -202,4 +215,57 @@ def attn_layer(q_bits, k_bits, v_bits, n_valid: int, wq_bits, wk_bits, eps: floa
                                 _ptr(wq), _ptr(wk), int(w_head_stride), float(eps),
                                 ctypes.byref(rope), float(scale), _ptr(rows), rows.size,
                                 threads or default_threads(), _ptr(out)), "attn_layer")
+    return out
+
+
+# ---- FP8 ("SAGE") variant
+
+
+def e4m3(x: float) -> float:
+    """Nearest FP8 E4M3 value of x (ties to even, saturating at +-448)."""
+    return lib().h3o_e4m3(float(x))
+
+
+def round_bf16(x: float) -> int:
+    """Bits of the nearest bf16 of x (ties to even)."""
+    return int(lib().h3o_round_bf16(float(x)))
+
+
+def quantize_group(x) -> tuple[np.ndarray, float]:
+    """One-scale FP8 quantization of fp32 values (decision in fp32): (codes, scale)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.size, dtype=np.float64)
+    scale = ctypes.c_double()
+    lib().h3o_quantize_group(_ptr(x), x.size, _ptr(codes), ctypes.byref(scale))
+    return codes.reshape(x.shape), scale.value
+
+
+def attn_varlen_fp8(q_bits, k_bits, v_bits, n_valid: int, scale: float, rows,
+                    threads: int | None = None) -> np.ndarray:
+    """FP8 attention over bf16 [S, H, D] buffers (Q/K already prepared) -> [R, H, D]."""
+    q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
+    S, H, D = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), dtype=np.float64)
+    _check(lib().h3o_attn_varlen_fp8(_ptr(q), _ptr(k), _ptr(v), S, int(n_valid), H, D, H * D,
+                                     float(scale), _ptr(rows), rows.size,
+                                     threads or default_threads(), _ptr(out)),
+           "attn_varlen_fp8")
+    return out
+
+
+def attn_layer_fp8(q_bits, k_bits, v_bits, n_valid: int, wq_bits, wk_bits, eps: float,
+                   rope: Rope, scale: float, rows, w_head_stride: int = 0,
+                   threads: int | None = None) -> np.ndarray:
+    """RMSNorm + RoPE (rounded to bf16) + FP8 attention over bf16 [S, H, D] buffers."""
+    q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
+    wq, wk = _u16(wq_bits), _u16(wk_bits)
+    S, H, D = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), dtype=np.float64)
+    _check(lib().h3o_attn_layer_fp8(_ptr(q), _ptr(k), _ptr(v), S, int(n_valid), H, D, H * D,
+                                    _ptr(wq), _ptr(wk), int(w_head_stride), float(eps),
+                                    ctypes.byref(rope), float(scale), _ptr(rows), rows.size,
+                                    threads or default_threads(), _ptr(out)),
+           "attn_layer_fp8")
     return out

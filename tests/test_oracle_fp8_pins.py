@@ -1,0 +1,234 @@
+"""Pins of the FP8 ("SAGE") oracle against definitions and closed forms, on the CPU.
+
+Page: "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH3 的实时服务"
+(Chinese translation of the vLLM blog post), §4.3 and figure 6: Q, K, P and V are
+quantized to FP8 for both attention products.  The format (OCP E4M3 "fn": bias 7,
+3 mantissa bits, subnormals, largest finite 448) is pinned by brute force over its 254
+finite values; the quantizer by its extremes and error bound and by a case where the
+fp32 and fp64 decisions differ; the attention by closed forms (equal keys, one key,
+power-of-two scaling of a V channel) and by its distance from exact attention.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+
+def e4m3_table():
+    """All finite E4M3 values as (value, code) with the code's 3 mantissa bits."""
+    out = []
+    for sign in (0, 1):
+        for e in range(16):
+            for m in range(8):
+                if e == 15 and m == 7:
+                    continue  # NaN
+                mag = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+                out.append(((-1) ** sign * mag, (sign << 7) | (e << 3) | m))
+    return out
+
+
+TABLE = e4m3_table()
+VALUES = np.array(sorted({v for v, _ in TABLE}))
+CODE_OF = {}
+for v, c in TABLE:
+    CODE_OF.setdefault(v, c)
+
+
+def nearest_e4m3(x):
+    """Brute force: the nearest finite E4M3 value, ties to the even code, saturating."""
+    if x >= 448:
+        return 448.0
+    if x <= -448:
+        return -448.0
+    d = np.abs(VALUES - x)
+    best = np.flatnonzero(d == d.min())
+    if len(best) == 1:
+        return float(VALUES[best[0]])
+    even = [VALUES[i] for i in best if CODE_OF[VALUES[i]] % 2 == 0]
+    return float(even[0])
+
+
+def test_every_finite_e4m3_value_maps_to_itself():
+    for v, _ in TABLE:
+        assert O.e4m3(v) == v, v
+    assert VALUES.max() == 448.0 and VALUES[VALUES > 0].min() == 2.0 ** -9
+
+
+def test_e4m3_midpoints_tie_to_even_and_saturate():
+    pos = VALUES[VALUES >= 0]
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = (a + b) / 2
+        want = a if CODE_OF[a] % 2 == 0 else b
+        assert O.e4m3(mid) == want, (a, b)
+        assert O.e4m3(-mid) == -want
+    for x in (448.0, 464.0, 500.0, 1e30):
+        assert O.e4m3(x) == 448.0 and O.e4m3(-x) == -448.0
+    assert math.isnan(O.e4m3(float("nan")))
+
+
+def test_e4m3_matches_brute_force_on_random_values():
+    rng = np.random.default_rng(3)
+    xs = np.concatenate([rng.standard_normal(3000) * s for s in (1e-3, 0.05, 1.0, 40.0, 300.0)])
+    for x in xs:
+        assert O.e4m3(float(x)) == nearest_e4m3(float(x)), x
+
+
+def test_round_bf16_matches_brute_force():
+    rng = np.random.default_rng(4)
+    xs = np.concatenate([rng.standard_normal(4000) * s for s in (1e-30, 1e-3, 1.0, 1e5)])
+    for x in xs:
+        b = int(np.array([x], dtype=np.float32).view(np.uint32)[0] >> 16)
+        cands = []
+        for c in (b - 1, b, b + 1):
+            val = float(np.array([c << 16], dtype=np.uint32).view(np.float32)[0])
+            cands.append((abs(val - x), c & 1, c))
+        cands.sort()
+        want = cands[0][2] if cands[0][0] < cands[1][0] else min(cands[:2], key=lambda t: t[1])[2]
+        assert O.round_bf16(float(x)) == want, x
+
+
+def test_quantize_group_extremes_zero_and_error_bound():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(500) * 3).astype(np.float32)
+    codes, scale = O.quantize_group(x)
+    i = int(np.argmax(np.abs(x)))
+    assert abs(codes[i]) == 448.0 and np.sign(codes[i]) == np.sign(x[i])
+    assert scale == pytest.approx(float(np.abs(x).max()) / 448.0, rel=0, abs=0)
+    deq = codes * scale
+    normal = np.abs(x) / scale >= 2.0 ** -6 * (1 + 1e-6)
+    assert np.all(np.abs(deq - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal] * (1 + 1e-6))
+    assert np.all(np.abs(deq - x)[~normal] <= 2.0 ** -10 * scale * (1 + 1e-6))
+    z, zs = O.quantize_group(np.zeros(7, dtype=np.float32))
+    assert zs == 0.0 and np.all(z == 0)
+
+
+def test_quantize_decision_taken_in_fp32():
+    """Values x whose fp32 product x * (448/amax) lands exactly on an E4M3 midpoint
+    (a tie, resolved to the even code) while the exact product 448 x / amax lies to one
+    side of it: the oracle must follow the fp32 product, the kernel's precision."""
+    amax = np.float32(3.7)
+    inv32 = np.float32(448.0) / amax
+    pos = VALUES[VALUES > 0]
+    found = 0
+    for a, b in zip(pos[:-1], pos[1:]):
+        t = (a + b) / 2
+        x0 = np.float32(t / float(inv32))
+        for step in range(-30, 31):
+            x = np.float32(x0)
+            for _ in range(abs(step)):
+                x = np.nextafter(x, np.float32(np.inf if step > 0 else -np.inf))
+            if not (0 < x < amax):
+                continue
+            y32 = float(np.float32(x) * inv32)
+            y_exact = float(x) * 448.0 / float(amax)
+            if y32 == t and nearest_e4m3(y_exact) != nearest_e4m3(y32):
+                codes, _ = O.quantize_group(np.array([amax, x], dtype=np.float32))
+                assert codes[1] == nearest_e4m3(y32), (x, y32, y_exact)
+                found += 1
+    assert found >= 3, found
+
+
+def bf16(x):
+    """bf16 bit patterns (RNE) of a float array."""
+    return np.array([O.round_bf16(float(v)) for v in np.ravel(x)], dtype=np.uint16).reshape(
+        np.shape(x))
+
+
+def test_equal_keys_give_mean_of_dequantized_values():
+    rng = np.random.default_rng(7)
+    S, N, H, D = 40, 37, 2, 128
+    q = bf16(rng.standard_normal((S, H, D)))
+    k = bf16(np.broadcast_to(rng.standard_normal((1, H, D)), (S, H, D)))
+    v = bf16(rng.standard_normal((S, H, D)))
+    out = O.attn_varlen_fp8(q, k, v, N, 1 / math.sqrt(D), np.arange(S))
+    vf = np.array(v.astype(np.uint32) << 16, dtype=np.uint32).view(np.float32)
+    for h in range(H):
+        for c in range(D):
+            codes, s = O.quantize_group(vf[:N, h, c])
+            assert np.allclose(out[:N, h, c], np.mean(codes) * s, rtol=1e-12, atol=1e-15)
+    assert np.all(out[N:] == 0)
+
+
+def test_single_key_returns_its_dequantized_value():
+    rng = np.random.default_rng(8)
+    S, H, D = 5, 3, 128
+    q, k, v = (bf16(rng.standard_normal((S, H, D))) for _ in range(3))
+    out = O.attn_varlen_fp8(q, k, v, 1, 0.088, np.array([0, 3]))
+    vf = np.array(v.astype(np.uint32) << 16, dtype=np.uint32).view(np.float32)
+    for h in range(H):
+        for c in range(D):
+            codes, s = O.quantize_group(vf[:1, h, c])
+            assert out[0, h, c] == codes[0] * s
+    assert np.all(out[1] == 0)
+
+
+def test_power_of_two_scaling_of_one_v_channel_is_isolated():
+    """Per-channel V scales: multiplying channel 5 by 2^10 multiplies its output by 2^10
+    exactly and leaves every other channel bit-identical."""
+    rng = np.random.default_rng(9)
+    S, N, H, D = 70, 70, 1, 128
+    q, k = bf16(rng.standard_normal((S, H, D))), bf16(rng.standard_normal((S, H, D)))
+    vv = rng.standard_normal((S, H, D))
+    v1 = bf16(vv)
+    vv2 = np.array(v1.astype(np.uint32) << 16, dtype=np.uint32).view(np.float32).astype(np.float64)
+    vv2[:, :, 5] *= 1024.0
+    v2 = bf16(vv2)
+    rows = np.arange(N)
+    a = O.attn_varlen_fp8(q, k, v1, N, 0.088, rows)
+    b = O.attn_varlen_fp8(q, k, v2, N, 0.088, rows)
+    assert np.array_equal(np.delete(a, 5, axis=2), np.delete(b, 5, axis=2))
+    assert np.array_equal(a[:, :, 5] * 1024.0, b[:, :, 5])
+
+
+def test_close_to_exact_attention_but_quantized():
+    """FP8 keeps 4 significant bits (per-element relative error up to 2^-4 in Q, K, P and
+    V), so the result must stay within 10 % relative L2 of exact attention on the same
+    bf16 inputs, and must differ from it (the quantization is really applied)."""
+    rng = np.random.default_rng(10)
+    S, N, H, D = 300, 290, 2, 128
+    q, k, v = (bf16(rng.standard_normal((S, H, D))) for _ in range(3))
+    rows = np.arange(N)
+    got = O.attn_varlen_fp8(q, k, v, N, 1 / math.sqrt(D), rows)
+    ref = O.attn_varlen(q, k, v, N, 1 / math.sqrt(D), rows)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 1e-3 < rel < 0.1, rel
+
+
+def test_layer_is_prologue_rounded_to_bf16_then_varlen():
+    rng = np.random.default_rng(11)
+    S, N, H, D = 48, 45, 2, 128
+    q, k, v = (bf16(rng.standard_normal((S, H, D))) for _ in range(3))
+    wq, wk = bf16(1 + 0.1 * rng.standard_normal(D)), bf16(1 + 0.1 * rng.standard_normal(D))
+    rope = O.make_rope(1e4, N)
+    rows = np.arange(S)
+    got = O.attn_layer_fp8(q, k, v, N, wq, wk, 1e-6, rope, 0.088, rows)
+    qn = np.zeros((S, H, D), dtype=np.uint16)
+    kn = np.zeros((S, H, D), dtype=np.uint16)
+    qn[:N] = bf16(O.prologue(q, N, wq, 1e-6, rope, np.arange(N)))
+    kn[:N] = bf16(O.prologue(k, N, wk, 1e-6, rope, np.arange(N)))
+    ref = O.attn_varlen_fp8(qn, kn, v, N, 0.088, rows)
+    assert np.array_equal(got, ref)
+
+
+def test_p_is_quantized_and_normalised_by_the_quantized_sum():
+    """Two keys in one K block, one channel: K rows (1, 0.5) quantize to exactly 448 and
+    224, Q = a e_0 to 448, so the scores are scale*a and scale*a/2.  With scale*a = 2 the
+    gap is 1: the weights are 256 and E4M3(256/e) = 96 (256/e = 94.2), and with V = (1, 0)
+    in every channel the output is exactly 256 / (256 + 96) (unquantized P would give
+    256 / (256 + 94.2))."""
+    S, N, H, D = 2, 2, 1, 128
+    scale = 0.088
+    a = 2.0 / scale
+    q = np.zeros((S, H, D))
+    q[:, 0, 0] = a
+    k = np.zeros((S, H, D))
+    k[0, 0, 0], k[1, 0, 0] = 1.0, 0.5
+    v = np.zeros((S, H, D))
+    v[0] = 1.0
+    qb, kb, vb = bf16(q), bf16(k), bf16(v)
+    a_b = float(np.array([int(qb[0, 0, 0]) << 16], dtype=np.uint32).view(np.float32)[0])
+    assert 92.0 <= 256.0 * math.exp(-scale * a_b / 2) < 100.0  # still rounds to 96
+    out = O.attn_varlen_fp8(qb, kb, vb, N, scale, np.array([0]))
+    assert np.allclose(out[0, 0], 256.0 / 352.0, rtol=1e-14, atol=0)
