@@ -19,9 +19,15 @@
 //     to +-448.  The quantization decision is taken in fp32 (inverse scale 448 / amax,
 //     one product, then rounding), the precision the kernel takes it in.
 //   - scores s_ij = scale * sq_i * sk_block(j) * sum_c Qq_ic Kq_jc (exact in fp64);
-//   - P_ij = E4M3(256 * exp(s_ij - max_j s_ij)); the row's largest weight is 256;
-//   - o_ic = sv_c * sum_j P_ij Vq_jc / sum_j P_ij (the normaliser is the sum of the
-//     quantized weights); rows in [N, S) are zero.
+//   - P is produced the way a streaming (online-softmax) attention produces it: the
+//     valid keys are taken in tiles of T consecutive keys (T = p_tile), a running row
+//     maximum m_t = max(m_(t-1), max over tile t of s_ij) is kept, the weights of tile t
+//     are P_ij = E4M3(256 * exp(s_ij - m_t)) (at most 256), and the sums of earlier
+//     tiles are carried over by the factor exp(m_(t-1) - m_t).  When a row's maximum
+//     lies in its first tile (or N <= T) this is P_ij = E4M3(256 exp(s_ij - max_j s_ij))
+//     for every key;
+//   - o_ic = sv_c * sum_j w_j P_ij Vq_jc / sum_j w_j P_ij with w_j = exp(m_t(j) - m_last)
+//     (the normaliser is the sum of the quantized weights); rows in [N, S) are zero.
 // Parity status: pinned by the closed forms in tests/test_oracle_fp8_pins.py.
 #include "h3_oracle.h"
 
@@ -126,10 +132,11 @@ uint16_t h3o_round_bf16(double x) {
 
 int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int64_t seq_buf, int64_t n_valid, int64_t heads, int64_t d,
-                        int64_t row_stride, double scale, const int64_t* rows, int64_t n_rows,
-                        int threads, double* out) {
+                        int64_t row_stride, double scale, int64_t p_tile, const int64_t* rows,
+                        int64_t n_rows, int threads, double* out) {
   if (!q || !k || !v || !out || (n_rows > 0 && !rows)) return H3O_ERR_ARG;
-  if (heads <= 0 || d <= 0 || n_valid < 0 || n_valid > seq_buf) return H3O_ERR_ARG;
+  if (heads <= 0 || d <= 0 || n_valid < 0 || n_valid > seq_buf || p_tile < 1)
+    return H3O_ERR_ARG;
   for (int64_t r = 0; r < n_rows; ++r)
     if (rows[r] < 0 || rows[r] >= seq_buf) return H3O_ERR_ARG;
   const int64_t N = n_valid;
@@ -167,19 +174,27 @@ int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         for (int64_t c = 0; c < d; ++c) qrow[(size_t)c] = (float)widen1(q[i * row_stride + h * d + c]);
         double sq;
         quantize(qrow.data(), d, qq.data(), &sq);
-        double m = -INFINITY;
         for (int64_t j = 0; j < N; ++j) {
           double dot = 0.0;
           for (int64_t c = 0; c < d; ++c) dot += qq[(size_t)c] * kq[(size_t)(j * d + c)];
           s[(size_t)j] = scale * sq * ks[(size_t)(j / 16)] * dot;
-          m = std::max(m, s[(size_t)j]);
         }
-        double l = 0.0;
+        // tiles of p_tile keys, running maximum, carried sums
+        double m = -INFINITY, l = 0.0;
         std::fill(acc.begin(), acc.end(), 0.0);
-        for (int64_t j = 0; j < N; ++j) {
-          const double p = h3o_e4m3(256.0 * std::exp(s[(size_t)j] - m));
-          l += p;
-          for (int64_t c = 0; c < d; ++c) acc[(size_t)c] += p * vq[(size_t)(j * d + c)];
+        for (int64_t t0 = 0; t0 < N; t0 += p_tile) {
+          const int64_t t1 = std::min(N, t0 + p_tile);
+          double mt = m;
+          for (int64_t j = t0; j < t1; ++j) mt = std::max(mt, s[(size_t)j]);
+          const double carry = (m == -INFINITY) ? 0.0 : std::exp(m - mt);
+          l *= carry;
+          for (int64_t c = 0; c < d; ++c) acc[(size_t)c] *= carry;
+          for (int64_t j = t0; j < t1; ++j) {
+            const double p = h3o_e4m3(256.0 * std::exp(s[(size_t)j] - mt));
+            l += p;
+            for (int64_t c = 0; c < d; ++c) acc[(size_t)c] += p * vq[(size_t)(j * d + c)];
+          }
+          m = mt;
         }
         for (int64_t c = 0; c < d; ++c) o[c] = vs[(size_t)c] * acc[(size_t)c] / l;
       }
@@ -191,8 +206,8 @@ int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_buf,
                        int64_t n_valid, int64_t heads, int64_t d, int64_t row_stride,
                        const uint16_t* w_q, const uint16_t* w_k, int64_t w_head_stride,
-                       double eps, const h3o_rope* rope, double scale, const int64_t* rows,
-                       int64_t n_rows, int threads, double* out) {
+                       double eps, const h3o_rope* rope, double scale, int64_t p_tile,
+                       const int64_t* rows, int64_t n_rows, int threads, double* out) {
   if (!q || !k || !v || !w_q || !w_k || !rope || !out) return H3O_ERR_ARG;
   if (heads <= 0 || d <= 0 || n_valid < 0 || n_valid > seq_buf) return H3O_ERR_ARG;
   // Normalised, rotated Q and K of every valid token, rounded to bf16 (the type the
@@ -215,7 +230,7 @@ int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   for (int64_t i = 0; i < N; ++i)
     for (int64_t c = 0; c < hd; ++c) vv[(size_t)(i * hd + c)] = v[i * row_stride + c];
   return h3o_attn_varlen_fp8(qn.data(), kn.data(), vv.data(), seq_buf, N, heads, d, hd, scale,
-                             rows, n_rows, threads, out);
+                             p_tile, rows, n_rows, threads, out);
 }
 
 }  // extern "C"

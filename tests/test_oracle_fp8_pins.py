@@ -232,3 +232,42 @@ def test_p_is_quantized_and_normalised_by_the_quantized_sum():
     assert 92.0 <= 256.0 * math.exp(-scale * a_b / 2) < 100.0  # still rounds to 96
     out = O.attn_varlen_fp8(qb, kb, vb, N, scale, np.array([0]))
     assert np.allclose(out[0, 0], 256.0 / 352.0, rtol=1e-14, atol=0)
+
+
+def test_streamed_p_equals_global_max_when_the_max_is_in_the_first_tile():
+    """The streamed weights use the running maximum of 64-key tiles; when every row's
+    largest score is at key 0 the running maximum is the row maximum from the first tile
+    on, so the result must equal the one-tile (global maximum) form bit for bit."""
+    rng = np.random.default_rng(12)
+    S, N, H, D = 200, 197, 2, 128
+    q = bf16(np.abs(rng.standard_normal((S, H, D))))
+    kk = 0.3 * rng.standard_normal((S, H, D))
+    kk[0] = 10.0  # the largest score of every (positive) query row
+    k = bf16(kk)
+    v = bf16(rng.standard_normal((S, H, D)))
+    rows = np.arange(N)
+    tiled = O.attn_varlen_fp8(q, k, v, N, 0.088, rows)
+    one_tile = O.attn_varlen_fp8(q, k, v, N, 0.088, rows, p_tile=10**9)
+    assert np.array_equal(tiled, one_tile)
+
+
+def test_streamed_p_two_tiles_closed_form():
+    """Keys 0-63 (tile 0) score 1, key 64 (tile 1) scores 2; V is 1 on key 64 and 0
+    elsewhere.  Tile 0's weights are quantized against its own maximum (256 each) and
+    carried over by e^-1, so o = 256 / (64 * 256 / e + 256) = 1 / (64 / e + 1) in every
+    channel; quantizing against the row maximum instead would give E4M3(256 / e) = 96
+    per key and o = 256 / (64 * 96 + 256) = 0.04."""
+    S, N, H, D = 65, 65, 1, 128
+    scale = 0.125
+    q = np.zeros((S, H, D))
+    q[:, 0, 0] = 8.0  # scale * q = 1
+    k = np.zeros((S, H, D))
+    k[:64, 0, 0] = 1.0
+    k[64, 0, 0] = 2.0
+    v = np.zeros((S, H, D))
+    v[64] = 1.0
+    out = O.attn_varlen_fp8(bf16(q), bf16(k), bf16(v), N, scale, np.array([0, 64]))
+    want = 1.0 / (64.0 / math.e + 1.0)
+    assert np.allclose(out, want, rtol=1e-12, atol=0)
+    glob = O.attn_varlen_fp8(bf16(q), bf16(k), bf16(v), N, scale, np.array([0]), p_tile=10**9)
+    assert np.allclose(glob, 0.04, rtol=1e-12, atol=0)
