@@ -11,7 +11,9 @@
  *           the structural tail padding is dropped; RoPE rows are built per token;
  *           heads are 128-channel projections of a 5,376-channel hidden state;
  *     §3.2  "融合的 DiT 算子": Q/K RMSNorm and RoPE are one fused operator;
- *     §3.5  speed-ups are "lossless" but not bitwise identical to other kernels.
+ *     §3.5  speed-ups are "lossless" but not bitwise identical to other kernels;
+ *     §4.3  (figure 6) SAGE attention: Q, K, P and V quantized to FP8 for both
+ *           attention products; the measured configuration is called "K16".
  *
  * ---------------------------------------------------------------------------
  * Conventions shared by every entry point
@@ -159,6 +161,57 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
                         const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
                         const h3_rope* rope, float softmax_scale, const h3_shape* shape,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * FP8 ("SAGE") attention  ([Blog §4.3], figure 6): the same attention with Q, K, P and
+ * V quantized to FP8 E4M3 (OCP "fn": largest finite 448, round to nearest even) for
+ * both products on the FP8 matrix cores.  The quantization groups (the reading of
+ * "K16"): one scale per Q row, per block of 16 consecutive keys, and per V channel over
+ * the N_b valid tokens, each per head; a group's scale is amax / 448, every element is
+ * multiplied by 448 / amax in fp32, clamped to +-448 and rounded.  The softmax weights
+ * are those of a streaming softmax over 64-key tiles: P = E4M3(256 exp(s - m_t)) with
+ * m_t the running row maximum through the key's tile, earlier sums carried over by
+ * exp(m_(t-1) - m_t); each row is normalised by the sum of its quantized weights.
+ * Products accumulate in fp32; output rounded to bf16.  Deterministic run to run.
+ * Accuracy: a few percent relative to exact attention (FP8 keeps 4 significant bits). */
+
+/* Workspace bytes of the FP8 calls: 64-key tiles of 19,456 bytes,
+ * B * H * ceil(S / 64) * 19456 bytes (about 0.59x the bf16 size of K plus V), then the
+ * per-channel V maxima, round_up(B * H * 128 * 4, 256) bytes.  0 if the shape is
+ * invalid. */
+size_t h3_attn_fp8_workspace_size(const h3_shape* shape);
+
+/* FP8 stage 1: quantize K (normalised and rotated first, rounded to bf16, when w_k is
+ * non-NULL, exactly as h3_kv_pack) and V of every batch into `workspace` as FP8 tiles
+ * with their scales.  Keys >= N_b are stored as zero codes.  Same arguments and errors
+ * as h3_kv_pack, with an FP8 workspace (h3_attn_fp8_workspace_size). */
+h3_status h3_kv_pack_fp8(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
+                         float eps, const h3_rope* rope, const h3_shape* shape, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* FP8 stage 2: attention of Q (normalised and rotated in registers when w_q is non-NULL,
+ * then quantized per row) against a workspace filled by h3_kv_pack_fp8 for the same
+ * shape, which is only read (calls sharing it may overlap).  Output rows [N_b, S) are
+ * zero.  Errors: as h3_kv_pack. */
+h3_status h3_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_head_stride,
+                             float eps, const h3_rope* rope, float softmax_scale,
+                             const h3_shape* shape, const void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* FP8 attention with Q and K already normalised and rotated: h3_kv_pack_fp8 (w_k NULL)
+ * then h3_attn_packed_fp8 (w_q NULL).  Arguments and errors as h3_attn_varlen, with an
+ * FP8 workspace. */
+h3_status h3_attn_varlen_fp8(const void* q, const void* k, const void* v, void* o,
+                             float softmax_scale, const h3_shape* shape, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* The whole layer in FP8: Q/K RMSNorm + RoPE fused (results rounded to bf16, as
+ * h3_qk_rmsnorm_rope writes them), then FP8 attention.  Arguments and errors as
+ * h3_attn_layer, with an FP8 workspace. */
+h3_status h3_attn_layer_fp8(const void* q, const void* k, const void* v, void* o,
+                            const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
+                            const h3_rope* rope, float softmax_scale, const h3_shape* shape,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -53,7 +53,9 @@ def make_rope(theta: float, n_1d: int, sections=(0, 0, 0), grid=(0, 0, 0)) -> Ro
 
 
 EXPORTED = ("h3_status_string", "h3_version", "h3_qk_rmsnorm_rope", "h3_attn_workspace_size",
-            "h3_kv_pack", "h3_attn_packed", "h3_attn_varlen", "h3_attn_layer")
+            "h3_kv_pack", "h3_attn_packed", "h3_attn_varlen", "h3_attn_layer",
+            "h3_attn_fp8_workspace_size", "h3_kv_pack_fp8", "h3_attn_packed_fp8",
+            "h3_attn_varlen_fp8", "h3_attn_layer_fp8")
 
 _lib = None
 
@@ -85,6 +87,16 @@ def lib():
         L.h3_attn_varlen.restype = ctypes.c_int
         L.h3_attn_layer.argtypes = [P, P, P, P, P, P, I64, F, RP, F, SH, P, SZ, P]
         L.h3_attn_layer.restype = ctypes.c_int
+        L.h3_attn_fp8_workspace_size.argtypes = [SH]
+        L.h3_attn_fp8_workspace_size.restype = SZ
+        L.h3_kv_pack_fp8.argtypes = [P, P, P, I64, F, RP, SH, P, SZ, P]
+        L.h3_kv_pack_fp8.restype = ctypes.c_int
+        L.h3_attn_packed_fp8.argtypes = [P, P, P, I64, F, RP, F, SH, P, SZ, P]
+        L.h3_attn_packed_fp8.restype = ctypes.c_int
+        L.h3_attn_varlen_fp8.argtypes = [P, P, P, P, F, SH, P, SZ, P]
+        L.h3_attn_varlen_fp8.restype = ctypes.c_int
+        L.h3_attn_layer_fp8.argtypes = [P, P, P, P, P, P, I64, F, RP, F, SH, P, SZ, P]
+        L.h3_attn_layer_fp8.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -140,14 +152,17 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def workspace_size(x: torch.Tensor) -> int:
-    """Workspace bytes an attention call on a tensor shaped like ``x`` needs."""
+def workspace_size(x: torch.Tensor, fp8: bool = False) -> int:
+    """Workspace bytes an attention call on a tensor shaped like ``x`` needs (``fp8``:
+    the FP8 calls)."""
     c = _Call(x, 0, x.shape[-2] * x.shape[-1], x.shape[-2] * x.shape[-1])
-    return int(lib().h3_attn_workspace_size(ctypes.byref(c.shape)))
+    f = lib().h3_attn_fp8_workspace_size if fp8 else lib().h3_attn_workspace_size
+    return int(f(ctypes.byref(c.shape)))
 
 
-def _workspace(q: torch.Tensor, call: _Call, workspace):
-    need = int(lib().h3_attn_workspace_size(ctypes.byref(call.shape)))
+def _workspace(q: torch.Tensor, call: _Call, workspace, fp8: bool = False):
+    f = lib().h3_attn_fp8_workspace_size if fp8 else lib().h3_attn_workspace_size
+    need = int(f(ctypes.byref(call.shape)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if workspace.numel() < need:
@@ -249,4 +264,78 @@ def attn_packed(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: floa
                                 ctypes.byref(rope) if rope is not None else None,
                                 float(softmax_scale), ctypes.byref(call.shape), _p(workspace),
                                 workspace.numel(), ctypes.c_void_p(st)), "h3_attn_packed")
+    return out
+
+
+def _qkv_strides(q, k, v, out):
+    s_in = _row_stride(q, "q")
+    for name, t in (("k", k), ("v", v)):
+        if _row_stride(t, name) != s_in:
+            raise ValueError("q, k and v must share a row stride")
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    return s_in, out, _row_stride(out, "out")
+
+
+def attn_varlen_fp8(q, k, v, n_valid, softmax_scale: float, out=None, workspace=None,
+                    stream=None):
+    """FP8 (SAGE) attention over the valid tokens with pre-normalised, pre-rotated Q/K
+    (h3_attn_varlen_fp8).  Output rows [N, S) are zero."""
+    s_in, out, s_out = _qkv_strides(q, k, v, out)
+    call = _Call(q, n_valid, s_in, s_out)
+    ws = _workspace(q, call, workspace, fp8=True)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_varlen_fp8(_p(q), _p(k), _p(v), _p(out), float(softmax_scale),
+                                    ctypes.byref(call.shape), _p(ws), ws.numel(),
+                                    ctypes.c_void_p(st)), "h3_attn_varlen_fp8")
+    return out
+
+
+def attn_layer_fp8(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_scale: float,
+                   out=None, workspace=None, stream=None):
+    """The whole layer with FP8 attention: Q/K RMSNorm + RoPE fused (h3_attn_layer_fp8)."""
+    s_in, out, s_out = _qkv_strides(q, k, v, out)
+    w_head_stride = 0 if w_q.dim() == 1 else w_q.stride(0)
+    call = _Call(q, n_valid, s_in, s_out)
+    ws = _workspace(q, call, workspace, fp8=True)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_layer_fp8(_p(q), _p(k), _p(v), _p(out), _p(w_q), _p(w_k),
+                                   w_head_stride, float(eps), ctypes.byref(rope),
+                                   float(softmax_scale), ctypes.byref(call.shape), _p(ws),
+                                   ws.numel(), ctypes.c_void_p(st)), "h3_attn_layer_fp8")
+    return out
+
+
+def kv_pack_fp8(k, v, n_valid, workspace=None, w_k=None, eps: float = 0.0,
+                rope: Rope | None = None, stream=None):
+    """FP8 stage 1 (h3_kv_pack_fp8): quantize K (normalised + rotated when ``w_k`` is
+    given) and V into FP8 tiles for h3_attn_packed_fp8.  Returns the workspace."""
+    s_in = _row_stride(k, "k")
+    if _row_stride(v, "v") != s_in:
+        raise ValueError("k and v must share a row stride")
+    call = _Call(k, n_valid, s_in, s_in)
+    ws = _workspace(k, call, workspace, fp8=True)
+    w_head_stride = 0 if (w_k is None or w_k.dim() == 1) else w_k.stride(0)
+    st = _stream(k.device) if stream is None else stream
+    _check(lib().h3_kv_pack_fp8(_p(k), _p(v), _p(w_k), w_head_stride, float(eps),
+                                ctypes.byref(rope) if rope is not None else None,
+                                ctypes.byref(call.shape), _p(ws), ws.numel(),
+                                ctypes.c_void_p(st)), "h3_kv_pack_fp8")
+    return ws
+
+
+def attn_packed_fp8(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: float = 0.0,
+                    rope: Rope | None = None, out=None, stream=None):
+    """FP8 stage 2 (h3_attn_packed_fp8): attention of ``q`` (normalised + rotated in
+    registers when ``w_q`` is given) against FP8 tiles packed by ``kv_pack_fp8``."""
+    s_in = _row_stride(q, "q")
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    s_out = _row_stride(out, "out")
+    call = _Call(q, n_valid, s_in, s_out)
+    w_head_stride = 0 if (w_q is None or w_q.dim() == 1) else w_q.stride(0)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_packed_fp8(_p(q), _p(out), _p(w_q), w_head_stride, float(eps),
+                                    ctypes.byref(rope) if rope is not None else None,
+                                    float(softmax_scale), ctypes.byref(call.shape),
+                                    _p(workspace), workspace.numel(), ctypes.c_void_p(st)),
+           "h3_attn_packed_fp8")
     return out

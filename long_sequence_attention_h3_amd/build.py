@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh3attn.so")
 SOURCES = [os.path.join(CSRC, "h3attn.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("common.hpp", "prologue.hpp", "attention.hpp")] + [
+HEADERS = [os.path.join(CSRC, f) for f in ("common.hpp", "prologue.hpp", "attention.hpp",
+                                                "attention_fp8.hpp")] + [
     os.path.join(ROOT, "include", "h3attn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

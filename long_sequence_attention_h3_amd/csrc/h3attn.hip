@@ -1,9 +1,11 @@
 // h3attn.hip — libh3attn: C ABI entry points (declared in include/h3attn.h), argument
-// validation and kernel launches.  Kernels live in prologue.hpp and attention.hpp.
+// validation and kernel launches.  Kernels live in prologue.hpp, attention.hpp and
+// attention_fp8.hpp.
 //
 // Pages: "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH3 的实时服务"
 // (Chinese translation of the vLLM blog post), §3.1 (valid-length attention over an
-// aligned packed buffer, per-token RoPE rows) and §3.2 (fused Q/K RMSNorm + RoPE).
+// aligned packed buffer, per-token RoPE rows), §3.2 (fused Q/K RMSNorm + RoPE) and §4.3
+// (the FP8 "SAGE" variant of the attention).
 #include "h3attn.h"
 
 #include <hip/hip_runtime.h>
@@ -13,6 +15,7 @@
 #include <cstring>
 
 #include "attention.hpp"
+#include "attention_fp8.hpp"
 #include "prologue.hpp"
 
 namespace {
@@ -124,8 +127,20 @@ h3_status launched() { return hipGetLastError() == hipSuccess ? H3_OK : H3_ERR_L
     if (st_ != H3_OK) return st_;      \
   } while (0)
 
-h3_status check_workspace(const h3_shape* s, const void* ws, size_t bytes) {
-  const size_t need = workspace_bytes(s);
+// FP8 workspace: tile images, [batch][head][tile] x fp8::kTileBytes, then the per-channel
+// V maxima, [batch][head][128] floats, rounded up to 256 bytes.
+size_t fp8_batch_img_bytes(const h3_shape* s) {
+  return (size_t)s->num_heads * (size_t)tiles_per_head(s) * (size_t)fp8::kTileBytes;
+}
+size_t fp8_vamax_words(const h3_shape* s) {
+  return (size_t)s->batch * (size_t)s->num_heads * kHeadDim;
+}
+size_t fp8_workspace_bytes(const h3_shape* s) {
+  return (size_t)s->batch * fp8_batch_img_bytes(s) + ((fp8_vamax_words(s) * 4 + 255) & ~size_t(255));
+}
+
+h3_status check_workspace(const h3_shape* s, const void* ws, size_t bytes, bool is_fp8 = false) {
+  const size_t need = is_fp8 ? fp8_workspace_bytes(s) : workspace_bytes(s);
   if (need > 0 && (!ws || bytes < need)) return H3_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return H3_ERR_ALIGN;
   return H3_OK;
@@ -228,6 +243,110 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
       attn_fwd_kernel<false, false><<<blocks, attn::kThreads, 0, stream>>>(aa);
       attn_fwd_kernel<false, true><<<blocks, attn::kThreads, 0, stream>>>(aa);
     }
+    H3_TRY(launched());
+  }
+  return H3_OK;
+}
+
+// ---------------------------------------------------------------- FP8 stage 1
+h3_status do_kv_pack_fp8(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
+                         float eps, const h3_rope* rope, const h3_shape* shp, void* workspace,
+                         size_t ws_bytes, hipStream_t stream) {
+  int64_t max_valid = 0;
+  H3_TRY(check_shape(shp, &max_valid));
+  if (!k || !v) return H3_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v)) return H3_ERR_ALIGN;
+  const bool norm = w_k != nullptr;
+  RopeArgs ra{};
+  if (norm) H3_TRY(check_norm(w_k, w_head_stride, eps, rope, max_valid, &ra));
+  H3_TRY(check_workspace(shp, workspace, ws_bytes, true));
+  H3_TRY(check_device());
+  const int64_t S = shp->seq_buf, tph = tiles_per_head(shp);
+  const int H = shp->num_heads;
+  const size_t per_batch = fp8_batch_img_bytes(shp);
+  uint32_t* vamax =
+      reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + shp->batch * per_batch);
+  const int64_t words = (int64_t)fp8_vamax_words(shp);
+  fill_zero_kernel<<<(unsigned)((words + 255) / 256), 256, 0, stream>>>(vamax, words);
+  H3_TRY(launched());
+  for (int b = 0; b < shp->batch; ++b) {
+    const int64_t n = shp->seq_valid[b];
+    if (n == 0) continue;
+    Fp8StatsArgs sa{};
+    sa.v = static_cast<const __bf16*>(v) + b * S * shp->in_row_stride;
+    sa.in_stride = shp->in_row_stride;
+    sa.n_valid = n;
+    sa.vamax = vamax + (int64_t)b * H * kHeadDim;
+    v_amax_kernel<<<dim3((unsigned)((n + kStatKeys - 1) / kStatKeys), (unsigned)H), 256, 0,
+                    stream>>>(sa);
+    H3_TRY(launched());
+    Fp8PackArgs pa{};
+    pa.k = static_cast<const __bf16*>(k) + b * S * shp->in_row_stride;
+    pa.v = sa.v;
+    pa.w_k = static_cast<const __bf16*>(w_k);
+    pa.w_head_stride = w_head_stride;
+    pa.in_stride = shp->in_row_stride;
+    pa.n_valid = n;
+    pa.tiles_per_head = tph;
+    pa.eps = eps;
+    pa.rope = ra;
+    pa.vamax = sa.vamax;
+    pa.img = static_cast<char*>(workspace) + b * per_batch;
+    const dim3 grid((unsigned)((n + kTileKeys - 1) / kTileKeys), (unsigned)H);
+    if (norm)
+      kv_pack_fp8_kernel<true><<<grid, 256, 0, stream>>>(pa);
+    else
+      kv_pack_fp8_kernel<false><<<grid, 256, 0, stream>>>(pa);
+    H3_TRY(launched());
+  }
+  return H3_OK;
+}
+
+// ---------------------------------------------------------------- FP8 stage 2
+h3_status do_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_head_stride,
+                             float eps, const h3_rope* rope, float softmax_scale,
+                             const h3_shape* shp, const void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+  int64_t max_valid = 0;
+  H3_TRY(check_shape(shp, &max_valid));
+  if (!q || !o) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  const bool norm = w_q != nullptr;
+  RopeArgs ra{};
+  if (norm) H3_TRY(check_norm(w_q, w_head_stride, eps, rope, max_valid, &ra));
+  H3_TRY(check_workspace(shp, workspace, ws_bytes, true));
+  H3_TRY(check_device());
+  const int H = shp->num_heads;
+  const int64_t S = shp->seq_buf;
+  if (S == 0) return H3_OK;
+  const int m_tiles = (int)((S + fp8::kRows - 1) / fp8::kRows);
+  const size_t per_batch = fp8_batch_img_bytes(shp);
+  const uint32_t* vamax = reinterpret_cast<const uint32_t*>(
+      static_cast<const char*>(workspace) + shp->batch * per_batch);
+  for (int b = 0; b < shp->batch; ++b) {
+    Fp8AttnArgs aa{};
+    aa.q = static_cast<const __bf16*>(q) + b * S * shp->in_row_stride;
+    aa.o = static_cast<__bf16*>(o) + b * S * shp->out_row_stride;
+    aa.img = static_cast<const char*>(workspace) + b * per_batch;
+    aa.vamax = vamax + (int64_t)b * H * kHeadDim;
+    aa.tiles_per_head = tiles_per_head(shp);
+    aa.in_stride = shp->in_row_stride;
+    aa.out_stride = shp->out_row_stride;
+    aa.n_valid = shp->seq_valid[b];
+    aa.seq_buf = S;
+    aa.heads = H;
+    aa.m_tiles = m_tiles;
+    aa.scale_log2 = softmax_scale * 1.4426950408889634f;
+    aa.w_q = static_cast<const __bf16*>(w_q);
+    aa.w_head_stride = w_head_stride;
+    aa.eps = eps;
+    aa.rope = ra;
+    const unsigned blocks = (unsigned)((int64_t)H * m_tiles);
+    if (norm)
+      attn_fp8_kernel<true><<<blocks, fp8::kThreads, 0, stream>>>(aa);
+    else
+      attn_fp8_kernel<false><<<blocks, fp8::kThreads, 0, stream>>>(aa);
     H3_TRY(launched());
   }
   return H3_OK;
@@ -339,6 +458,53 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
                     stream));
   return do_attn_packed(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape, workspace,
                         workspace_bytes_, stream);
+}
+
+size_t h3_attn_fp8_workspace_size(const h3_shape* shape) {
+  int64_t max_valid = 0;
+  if (check_shape(shape, &max_valid) != H3_OK) return 0;
+  return fp8_workspace_bytes(shape);
+}
+
+h3_status h3_kv_pack_fp8(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
+                         float eps, const h3_rope* rope, const h3_shape* shape, void* workspace,
+                         size_t workspace_bytes_, hipStream_t stream) {
+  return do_kv_pack_fp8(k, v, w_k, w_head_stride, eps, rope, shape, workspace,
+                        workspace_bytes_, stream);
+}
+
+h3_status h3_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_head_stride,
+                             float eps, const h3_rope* rope, float softmax_scale,
+                             const h3_shape* shape, const void* workspace,
+                             size_t workspace_bytes_, hipStream_t stream) {
+  return do_attn_packed_fp8(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape,
+                            workspace, workspace_bytes_, stream);
+}
+
+h3_status h3_attn_varlen_fp8(const void* q, const void* k, const void* v, void* o,
+                             float softmax_scale, const h3_shape* shape, void* workspace,
+                             size_t workspace_bytes_, hipStream_t stream) {
+  if (!q || !o) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  H3_TRY(do_kv_pack_fp8(k, v, nullptr, 0, 0.0f, nullptr, shape, workspace, workspace_bytes_,
+                        stream));
+  return do_attn_packed_fp8(q, o, nullptr, 0, 0.0f, nullptr, softmax_scale, shape, workspace,
+                            workspace_bytes_, stream);
+}
+
+h3_status h3_attn_layer_fp8(const void* q, const void* k, const void* v, void* o,
+                            const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
+                            const h3_rope* rope, float softmax_scale, const h3_shape* shape,
+                            void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+  if (!q || !o || !w_q || !w_k) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  H3_TRY(check_weights(w_q, w_k, w_head_stride));
+  H3_TRY(do_kv_pack_fp8(k, v, w_k, w_head_stride, eps, rope, shape, workspace,
+                        workspace_bytes_, stream));
+  return do_attn_packed_fp8(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape,
+                            workspace, workspace_bytes_, stream);
 }
 
 }  // extern "C"
