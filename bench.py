@@ -11,13 +11,18 @@ inputs already resident in HBM.  Prints one JSON line:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload
              (sampled query rows of every head), whose rows also gate parity
   kernels    the other kernels' achieved bandwidth (K/V pre-pass, standalone prologue)
+  fp8        the FP8 (SAGE) variant on the same workload: h3_attn_layer_fp8 per step, its
+             attention kernel alone (h3_attn_packed_fp8) against the FP8 dense MFMA peak,
+             and its pre-pass; reported beside the bf16 headline, never as `value`
   per_workload  every workload size: h3_attn_layer and h3_attn_varlen TFLOP/s (median and
-             min of 10 calls after 3 warm-up calls) and h3_qk_rmsnorm_rope GB/s
+             min of 10 calls after 3 warm-up calls), the same for the FP8 calls, and
+             h3_qk_rmsnorm_rope GB/s
   sclk_mhz   the shader clock the driver reported right after the timed region
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
        python bench.py --only attn   (K/V pre-pass once, then K attention launches only:
                                       the run the hardware counters are read from)
+       python bench.py --only attn_fp8  (the same for the FP8 attention kernel)
        python bench.py --only copy   (K copies of a 2 GiB buffer: a plain copy kernel of
                                       known size that calibrates those counters)
 """
@@ -37,35 +42,38 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s + % bf16 MFMA peak, 42 heads x 58,758 valid tokens, 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = ("long_sequence_attention_h3_amd/csrc/attention.hpp",
                   "long_sequence_attention_h3_amd/csrc/common.hpp",
                   "long_sequence_attention_h3_amd/csrc/prologue.hpp",
                   "long_sequence_attention_h3_amd/csrc/h3attn.hip")
+FP8_KERNEL_SOURCES = KERNEL_SOURCES + ("long_sequence_attention_h3_amd/csrc/attention_fp8.hpp",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fp8_traffic.json")
 
 
 def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_units: float):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or
+def measured_traffic(path: str = TRAFFIC_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per attention launch from a committed rocprofv3 counter summary, or
     None when there is none or the kernel sources changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash(sources):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -122,6 +130,7 @@ def per_workload(torch, B, W, dev, stream):
         n = d["n_valid"]
         out = torch.empty_like(d["q"])
         ws = torch.empty(B.workspace_size(d["q"]), dtype=torch.uint8, device=dev)
+        ws8 = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
         q2, k2 = torch.empty_like(d["q"]), torch.empty_like(d["k"])
         row = {"heads": w.heads, "n_valid": w.n_valid, "seq_buf": w.seq_buf,
                "flop": w.flops}
@@ -130,6 +139,11 @@ def per_workload(torch, B, W, dev, stream):
                                                   w.eps, rope, scale, out=out, workspace=ws),
             "h3_attn_varlen": lambda: B.attn_varlen(d["q"], d["k"], d["v"], n, scale, out=out,
                                                     workspace=ws),
+            "h3_attn_layer_fp8": lambda: B.attn_layer_fp8(d["q"], d["k"], d["v"], d["w_q"],
+                                                          d["w_k"], n, w.eps, rope, scale,
+                                                          out=out, workspace=ws8),
+            "h3_attn_varlen_fp8": lambda: B.attn_varlen_fp8(d["q"], d["k"], d["v"], n, scale,
+                                                            out=out, workspace=ws8),
         }
         for name, fn in calls.items():
             t = call_times(torch, stream, fn)
@@ -146,9 +160,10 @@ def per_workload(torch, B, W, dev, stream):
                                      "GB/s": round(nbytes / med / 1e6, 1)}
         table[w.name] = row
         log(f"[bench] {w.name}: layer {row['h3_attn_layer']['tflops_median']} TFLOP/s, varlen "
-            f"{row['h3_attn_varlen']['tflops_median']} TFLOP/s, prologue "
+            f"{row['h3_attn_varlen']['tflops_median']} TFLOP/s, layer_fp8 "
+            f"{row['h3_attn_layer_fp8']['tflops_median']} TFLOP/s, prologue "
             f"{row['h3_qk_rmsnorm_rope']['GB/s']} GB/s")
-        del d, out, ws, q2, k2
+        del d, out, ws, ws8, q2, k2
         torch.cuda.empty_cache()
     return table
 
@@ -174,7 +189,7 @@ def main() -> int:
     ap.add_argument("--cpu-rows-per-head", type=int, default=4096)
     ap.add_argument("--no-per-workload", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("all", "attn", "copy"), default="all")
+    ap.add_argument("--only", choices=("all", "attn", "attn_fp8", "copy"), default="all")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the layer is "
@@ -217,6 +232,15 @@ def main() -> int:
             B.attn_packed(d["q"], ws, n, scale, w_q=d["w_q"], eps=w.eps, rope=rope, out=out)
             torch.cuda.synchronize()
             log(f"[bench] attention launch {i + 1}/{args.steps} done")
+        return 0
+    if args.only == "attn_fp8":
+        ws8 = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
+        B.kv_pack_fp8(d["k"], d["v"], n, workspace=ws8, w_k=d["w_k"], eps=w.eps, rope=rope)
+        for i in range(args.steps):
+            B.attn_packed_fp8(d["q"], ws8, n, scale, w_q=d["w_q"], eps=w.eps, rope=rope,
+                              out=out)
+            torch.cuda.synchronize()
+            log(f"[bench] fp8 attention launch {i + 1}/{args.steps} done")
         return 0
 
     # ---- headline: K whole-layer steps
@@ -281,7 +305,40 @@ def main() -> int:
     log(f"[bench] kv_pack {ms_pack:.3f} ms ({pack_bytes / ms_pack / 1e6:.0f} GB/s), "
         f"qk_rmsnorm_rope {ms_prol:.3f} ms ({prol_bytes / ms_prol / 1e6:.0f} GB/s)")
 
-    traffic = measured_traffic(1.0)
+    # ---- the FP8 (SAGE) variant on the same workload
+    ws8 = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
+    out8 = torch.empty_like(d["q"])
+    ms_layer8 = timed(lambda: B.attn_layer_fp8(d["q"], d["k"], d["v"], d["w_q"], d["w_k"], n,
+                                               w.eps, rope, scale, out=out8, workspace=ws8),
+                      args.steps)
+    ms_pack8 = timed(lambda: B.kv_pack_fp8(d["k"], d["v"], n, workspace=ws8, w_k=d["w_k"],
+                                           eps=w.eps, rope=rope), args.steps)
+    ms_attn8 = timed(lambda: B.attn_packed_fp8(d["q"], ws8, n, scale, w_q=d["w_q"], eps=w.eps,
+                                               rope=rope, out=out8), args.steps)
+    pack8_bytes = 3 * w.n_valid * row_bytes + w.heads * tiles * 19456
+    fp8 = {
+        "entry": "h3_attn_layer_fp8",
+        "dtype": "fp8 e4m3 products, fp32 accumulation, bf16 in/out",
+        "ms_per_step": round(ms_layer8, 4),
+        "tflops": round(flops / ms_layer8 / 1e9, 2),
+        "speedup_over_bf16_step": round(ms_step / ms_layer8, 3),
+        "attention_kernel": {"kernel": "attn_fp8_kernel", "ms": round(ms_attn8, 4),
+                             "tflops": round(flops / ms_attn8 / 1e9, 2),
+                             "frac_fp8_peak": round(flops / ms_attn8 / 1e9 / PEAK_FP8_TFLOPS, 4),
+                             "peak": PEAK_FP8_TFLOPS,
+                             "traffic": measured_traffic(FP8_TRAFFIC_FILE, FP8_KERNEL_SOURCES),
+                             "source_hash": source_hash(FP8_KERNEL_SOURCES)},
+        "pre_pass": {"kernels": "fill_zero_kernel + v_amax_kernel + kv_pack_fp8_kernel",
+                     "ms": round(ms_pack8, 4), "bytes": pack8_bytes,
+                     "GB/s": round(pack8_bytes / ms_pack8 / 1e6, 1)},
+    }
+    log(f"[bench] h3_attn_layer_fp8 {ms_layer8:.3f} ms/step ({fp8['tflops']} TFLOP/s), "
+        f"attn_fp8_kernel {ms_attn8:.3f} ms ({fp8['attention_kernel']['tflops']} TFLOP/s, "
+        f"{100 * fp8['attention_kernel']['frac_fp8_peak']:.1f}% of fp8 peak), pre-pass "
+        f"{ms_pack8:.3f} ms")
+    del ws8, out8
+
+    traffic = measured_traffic()
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -315,6 +372,7 @@ def main() -> int:
                                     "frac_hbm": round(prol_bytes / ms_prol / 1e6 /
                                                       PEAK_HBM_GBS, 4)},
         },
+        "fp8": fp8,
         "wall_s_timed_region": round(wall, 4),
         "sclk_mhz": sclk,
         "source_hash": source_hash(),
