@@ -125,18 +125,21 @@ void h3o_quantize_group(const float* x, int64_t n, double* codes, double* scale)
 
 /* FP8 attention on bf16 buffers whose Q and K are already normalised and rotated
  * (same layouts and row semantics as h3o_attn_varlen); the weights P are quantized
- * against the running row maximum of tiles of p_tile keys. */
+ * against the running row maximum of tiles of p_tile keys; with skip_threshold > 0 a
+ * tile whose maximum is below the running maximum by a factor under skip_threshold
+ * is dropped for that row (Skip-Softmax). */
 int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int64_t seq_buf, int64_t n_valid, int64_t heads, int64_t d,
-                        int64_t row_stride, double scale, int64_t p_tile, const int64_t* rows,
-                        int64_t n_rows, int threads, double* out);
+                        int64_t row_stride, double scale, int64_t p_tile, double skip_threshold,
+                        const int64_t* rows, int64_t n_rows, int threads, double* out);
 
 /* The FP8 layer: prologue of Q and K (fp64, rounded to bf16), then h3o_attn_varlen_fp8. */
 int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_buf,
                        int64_t n_valid, int64_t heads, int64_t d, int64_t row_stride,
                        const uint16_t* w_q, const uint16_t* w_k, int64_t w_head_stride,
                        double eps, const h3o_rope* rope, double scale, int64_t p_tile,
-                       const int64_t* rows, int64_t n_rows, int threads, double* out);
+                       double skip_threshold, const int64_t* rows, int64_t n_rows, int threads,
+                       double* out);
 
 #ifdef __cplusplus
 }

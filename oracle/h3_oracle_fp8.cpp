@@ -28,6 +28,12 @@
 //     for every key;
 //   - o_ic = sv_c * sum_j w_j P_ij Vq_jc / sum_j w_j P_ij with w_j = exp(m_t(j) - m_last)
 //     (the normaliser is the sum of the quantized weights); rows in [N, S) are zero.
+//   - Skip-Softmax (same section: a tile-level decision taken from the QK result drops
+//     the softmax and P V work of unimportant tiles; a higher threshold skips more):
+//     with threshold lambda in [0, 1), tile t (t >= 1) is dropped for row i when
+//     exp(max over the tile of s_ij - m_(t-1)) < lambda, m_(t-1) being the running
+//     maximum before the tile; a dropped tile adds nothing and leaves the maximum as
+//     it is.  lambda = 0 never drops a tile.  The decision is per query row.
 // Parity status: pinned by the closed forms in tests/test_oracle_fp8_pins.py.
 #include "h3_oracle.h"
 
@@ -132,11 +138,12 @@ uint16_t h3o_round_bf16(double x) {
 
 int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int64_t seq_buf, int64_t n_valid, int64_t heads, int64_t d,
-                        int64_t row_stride, double scale, int64_t p_tile, const int64_t* rows,
-                        int64_t n_rows, int threads, double* out) {
+                        int64_t row_stride, double scale, int64_t p_tile, double skip_threshold,
+                        const int64_t* rows, int64_t n_rows, int threads, double* out) {
   if (!q || !k || !v || !out || (n_rows > 0 && !rows)) return H3O_ERR_ARG;
   if (heads <= 0 || d <= 0 || n_valid < 0 || n_valid > seq_buf || p_tile < 1)
     return H3O_ERR_ARG;
+  if (!(skip_threshold >= 0.0 && skip_threshold < 1.0)) return H3O_ERR_ARG;
   for (int64_t r = 0; r < n_rows; ++r)
     if (rows[r] < 0 || rows[r] >= seq_buf) return H3O_ERR_ARG;
   const int64_t N = n_valid;
@@ -184,8 +191,10 @@ int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         std::fill(acc.begin(), acc.end(), 0.0);
         for (int64_t t0 = 0; t0 < N; t0 += p_tile) {
           const int64_t t1 = std::min(N, t0 + p_tile);
-          double mt = m;
-          for (int64_t j = t0; j < t1; ++j) mt = std::max(mt, s[(size_t)j]);
+          double local = -INFINITY;
+          for (int64_t j = t0; j < t1; ++j) local = std::max(local, s[(size_t)j]);
+          if (m != -INFINITY && std::exp(local - m) < skip_threshold) continue;  // dropped
+          const double mt = std::max(m, local);
           const double carry = (m == -INFINITY) ? 0.0 : std::exp(m - mt);
           l *= carry;
           for (int64_t c = 0; c < d; ++c) acc[(size_t)c] *= carry;
@@ -207,7 +216,8 @@ int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        int64_t n_valid, int64_t heads, int64_t d, int64_t row_stride,
                        const uint16_t* w_q, const uint16_t* w_k, int64_t w_head_stride,
                        double eps, const h3o_rope* rope, double scale, int64_t p_tile,
-                       const int64_t* rows, int64_t n_rows, int threads, double* out) {
+                       double skip_threshold, const int64_t* rows, int64_t n_rows, int threads,
+                       double* out) {
   if (!q || !k || !v || !w_q || !w_k || !rope || !out) return H3O_ERR_ARG;
   if (heads <= 0 || d <= 0 || n_valid < 0 || n_valid > seq_buf) return H3O_ERR_ARG;
   // Normalised, rotated Q and K of every valid token, rounded to bf16 (the type the
@@ -230,7 +240,7 @@ int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   for (int64_t i = 0; i < N; ++i)
     for (int64_t c = 0; c < hd; ++c) vv[(size_t)(i * hd + c)] = v[i * row_stride + c];
   return h3o_attn_varlen_fp8(qn.data(), kn.data(), vv.data(), seq_buf, N, heads, d, hd, scale,
-                             p_tile, rows, n_rows, threads, out);
+                             p_tile, skip_threshold, rows, n_rows, threads, out);
 }
 
 }  // extern "C"

@@ -271,3 +271,65 @@ def test_streamed_p_two_tiles_closed_form():
     assert np.allclose(out, want, rtol=1e-12, atol=0)
     glob = O.attn_varlen_fp8(bf16(q), bf16(k), bf16(v), N, scale, np.array([0]), p_tile=10**9)
     assert np.allclose(glob, 0.04, rtol=1e-12, atol=0)
+
+
+def _one_channel_case(n, kvals, vvals, scale=0.125):
+    """Q = 8 e_0 (scale * q = 1), K = k_j e_0 (score k_j), V = v_j in every channel."""
+    S, H, D = n, 1, 128
+    q = np.zeros((S, H, D))
+    q[:, 0, 0] = 8.0
+    k = np.zeros((S, H, D))
+    k[:, 0, 0] = kvals
+    v = np.broadcast_to(np.asarray(vvals, dtype=np.float64)[:, None, None], (S, H, D)).copy()
+    return bf16(q), bf16(k), bf16(v), scale
+
+
+def test_skip_threshold_zero_is_dense():
+    rng = np.random.default_rng(13)
+    S, N, H, D = 200, 190, 2, 128
+    q, k, v = (bf16(rng.standard_normal((S, H, D)) * s) for s in (3.0, 1.0, 1.0))
+    rows = np.arange(N)
+    dense = O.attn_varlen_fp8(q, k, v, N, 0.088, rows)
+    assert np.array_equal(O.attn_varlen_fp8(q, k, v, N, 0.088, rows, skip_threshold=0.0), dense)
+    with pytest.raises(ValueError):
+        O.attn_varlen_fp8(q, k, v, N, 0.088, rows, skip_threshold=1.0)
+
+
+def test_skip_single_key_tile_threshold_sides():
+    """Tile 0: 64 keys of score 1 and V = 0; tile 1: one key of score 0 and V = 1.  Its
+    factor against the running maximum is e^-1 = 0.3679: a threshold above it drops the
+    tile (output exactly 0), one below keeps it (weight E4M3(256/e) = 96, output
+    96 / (64 * 256 + 96))."""
+    kv = [1.0] * 64 + [0.0]
+    vv = [0.0] * 64 + [1.0]
+    q, k, v, scale = _one_channel_case(65, kv, vv)
+    rows = np.array([0, 64])
+    dropped = O.attn_varlen_fp8(q, k, v, 65, scale, rows, skip_threshold=0.37)
+    kept = O.attn_varlen_fp8(q, k, v, 65, scale, rows, skip_threshold=0.36)
+    assert np.all(dropped == 0.0)
+    assert np.allclose(kept, 96.0 / (64 * 256 + 96), rtol=1e-12, atol=0)
+
+
+def test_skip_never_drops_a_tile_that_raises_the_maximum():
+    kv = [1.0] * 64 + [2.0]
+    vv = [0.0] * 64 + [1.0]
+    q, k, v, scale = _one_channel_case(65, kv, vv)
+    out = O.attn_varlen_fp8(q, k, v, 65, scale, np.array([0]), skip_threshold=0.99)
+    assert np.allclose(out, 1.0 / (64.0 / math.e + 1.0), rtol=1e-12, atol=0)
+
+
+def test_skip_decides_against_the_running_maximum_before_the_tile():
+    """Tiles of scores 1 (V = 1), 0 (V = 0) and one key of score 3 (V = 0), threshold 0.5.
+    Tile 1 is dropped (e^-1 < 0.5 against the running maximum 1); tile 0 is kept although
+    it is e^-2 below the row maximum, so o = 64 e^-2 / (64 e^-2 + 1).  Keeping tile 1
+    would add 64 * 96 e^-2 to the normaliser; judging tile 0 against the row maximum
+    would drop it and give 0."""
+    kv = [1.0] * 64 + [0.0] * 64 + [3.0]
+    vv = [1.0] * 64 + [0.0] * 65
+    q, k, v, scale = _one_channel_case(129, kv, vv)
+    out = O.attn_varlen_fp8(q, k, v, 129, scale, np.array([5]), skip_threshold=0.5)
+    e2 = math.exp(-2.0)
+    assert np.allclose(out, 64 * e2 / (64 * e2 + 1.0), rtol=1e-12, atol=0)
+    dense = O.attn_varlen_fp8(q, k, v, 129, scale, np.array([5]))
+    assert np.allclose(dense, 64 * 256 * e2 / (64 * 256 * e2 + 64 * 96 * e2 + 256),
+                       rtol=1e-12, atol=0)
