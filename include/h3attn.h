@@ -173,12 +173,23 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
  * m_t the running row maximum through the key's tile, earlier sums carried over by
  * exp(m_(t-1) - m_t); each row is normalised by the sum of its quantized weights.
  * Products accumulate in fp32; output rounded to bf16.  Deterministic run to run.
- * Accuracy: a few percent relative to exact attention (FP8 keeps 4 significant bits). */
+ * Accuracy: a few percent relative to exact attention (FP8 keeps 4 significant bits).
+ *
+ * Skip-Softmax ([Blog §4.3], figure 6: a tile-level decision from the QK result skips
+ * the softmax and P x V work of unimportant tiles; a higher threshold skips more):
+ * skip_threshold in [0, 1).  For each query row, a 64-key tile after the first is
+ * dropped when exp(tile maximum - running maximum before the tile) < skip_threshold
+ * (scores s = softmax_scale * q . k); a dropped tile contributes nothing.  The result
+ * depends only on each row's own scores (not on how rows are grouped); work is saved
+ * where all 32 rows of a wave drop a tile.  0 disables it (dense FP8 attention). */
 
 /* Workspace bytes of the FP8 calls: 64-key tiles of 19,456 bytes,
  * B * H * ceil(S / 64) * 19456 bytes (about 0.59x the bf16 size of K plus V), then the
- * per-channel V maxima, round_up(B * H * 128 * 4, 256) bytes.  0 if the shape is
- * invalid. */
+ * per-channel V maxima, round_up(B * H * 128 * 4, 256) bytes, then the skip counts,
+ * round_up(B * H * ceil(S / 256) * 4, 256) bytes: one uint32 per 256 query rows of each
+ * head and batch, in that order ([batch][head][row block]), holding the number of
+ * (32-row x 64-key) tiles whose work the last h3_attn_packed_fp8 call on this
+ * workspace skipped (0 without Skip-Softmax).  0 if the shape is invalid. */
 size_t h3_attn_fp8_workspace_size(const h3_shape* shape);
 
 /* FP8 stage 1: quantize K (normalised and rotated first, rounded to bf16, when w_k is
@@ -191,27 +202,30 @@ h3_status h3_kv_pack_fp8(const void* k, const void* v, const void* w_k, int64_t 
 
 /* FP8 stage 2: attention of Q (normalised and rotated in registers when w_q is non-NULL,
  * then quantized per row) against a workspace filled by h3_kv_pack_fp8 for the same
- * shape, which is only read (calls sharing it may overlap).  Output rows [N_b, S) are
- * zero.  Errors: as h3_kv_pack. */
+ * shape, with Skip-Softmax threshold skip_threshold (0: dense).  The tile images are
+ * only read; the skip counts after them are written, so two calls sharing one
+ * workspace must not overlap in time.  Output rows [N_b, S) are zero.
+ * Errors: as h3_kv_pack; H3_ERR_SHAPE for skip_threshold outside [0, 1). */
 h3_status h3_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_head_stride,
                              float eps, const h3_rope* rope, float softmax_scale,
-                             const h3_shape* shape, const void* workspace,
+                             float skip_threshold, const h3_shape* shape, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
 /* FP8 attention with Q and K already normalised and rotated: h3_kv_pack_fp8 (w_k NULL)
  * then h3_attn_packed_fp8 (w_q NULL).  Arguments and errors as h3_attn_varlen, with an
- * FP8 workspace. */
+ * FP8 workspace and the Skip-Softmax threshold (0: dense). */
 h3_status h3_attn_varlen_fp8(const void* q, const void* k, const void* v, void* o,
-                             float softmax_scale, const h3_shape* shape, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream);
+                             float softmax_scale, float skip_threshold, const h3_shape* shape,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The whole layer in FP8: Q/K RMSNorm + RoPE fused (results rounded to bf16, as
  * h3_qk_rmsnorm_rope writes them), then FP8 attention.  Arguments and errors as
- * h3_attn_layer, with an FP8 workspace. */
+ * h3_attn_layer, with an FP8 workspace and the Skip-Softmax threshold (0: dense). */
 h3_status h3_attn_layer_fp8(const void* q, const void* k, const void* v, void* o,
                             const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
-                            const h3_rope* rope, float softmax_scale, const h3_shape* shape,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+                            const h3_rope* rope, float softmax_scale, float skip_threshold,
+                            const h3_shape* shape, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -91,11 +91,11 @@ def lib():
         L.h3_attn_fp8_workspace_size.restype = SZ
         L.h3_kv_pack_fp8.argtypes = [P, P, P, I64, F, RP, SH, P, SZ, P]
         L.h3_kv_pack_fp8.restype = ctypes.c_int
-        L.h3_attn_packed_fp8.argtypes = [P, P, P, I64, F, RP, F, SH, P, SZ, P]
+        L.h3_attn_packed_fp8.argtypes = [P, P, P, I64, F, RP, F, F, SH, P, SZ, P]
         L.h3_attn_packed_fp8.restype = ctypes.c_int
-        L.h3_attn_varlen_fp8.argtypes = [P, P, P, P, F, SH, P, SZ, P]
+        L.h3_attn_varlen_fp8.argtypes = [P, P, P, P, F, F, SH, P, SZ, P]
         L.h3_attn_varlen_fp8.restype = ctypes.c_int
-        L.h3_attn_layer_fp8.argtypes = [P, P, P, P, P, P, I64, F, RP, F, SH, P, SZ, P]
+        L.h3_attn_layer_fp8.argtypes = [P, P, P, P, P, P, I64, F, RP, F, F, SH, P, SZ, P]
         L.h3_attn_layer_fp8.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -277,21 +277,22 @@ def _qkv_strides(q, k, v, out):
 
 
 def attn_varlen_fp8(q, k, v, n_valid, softmax_scale: float, out=None, workspace=None,
-                    stream=None):
+                    stream=None, skip_threshold: float = 0.0):
     """FP8 (SAGE) attention over the valid tokens with pre-normalised, pre-rotated Q/K
-    (h3_attn_varlen_fp8).  Output rows [N, S) are zero."""
+    (h3_attn_varlen_fp8), with optional Skip-Softmax.  Output rows [N, S) are zero."""
     s_in, out, s_out = _qkv_strides(q, k, v, out)
     call = _Call(q, n_valid, s_in, s_out)
     ws = _workspace(q, call, workspace, fp8=True)
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_varlen_fp8(_p(q), _p(k), _p(v), _p(out), float(softmax_scale),
-                                    ctypes.byref(call.shape), _p(ws), ws.numel(),
+                                    float(skip_threshold), ctypes.byref(call.shape), _p(ws),
+                                    ws.numel(),
                                     ctypes.c_void_p(st)), "h3_attn_varlen_fp8")
     return out
 
 
 def attn_layer_fp8(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_scale: float,
-                   out=None, workspace=None, stream=None):
+                   out=None, workspace=None, stream=None, skip_threshold: float = 0.0):
     """The whole layer with FP8 attention: Q/K RMSNorm + RoPE fused (h3_attn_layer_fp8)."""
     s_in, out, s_out = _qkv_strides(q, k, v, out)
     w_head_stride = 0 if w_q.dim() == 1 else w_q.stride(0)
@@ -300,8 +301,9 @@ def attn_layer_fp8(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_s
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_layer_fp8(_p(q), _p(k), _p(v), _p(out), _p(w_q), _p(w_k),
                                    w_head_stride, float(eps), ctypes.byref(rope),
-                                   float(softmax_scale), ctypes.byref(call.shape), _p(ws),
-                                   ws.numel(), ctypes.c_void_p(st)), "h3_attn_layer_fp8")
+                                   float(softmax_scale), float(skip_threshold),
+                                   ctypes.byref(call.shape), _p(ws), ws.numel(),
+                                   ctypes.c_void_p(st)), "h3_attn_layer_fp8")
     return out
 
 
@@ -324,7 +326,8 @@ def kv_pack_fp8(k, v, n_valid, workspace=None, w_k=None, eps: float = 0.0,
 
 
 def attn_packed_fp8(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: float = 0.0,
-                    rope: Rope | None = None, out=None, stream=None):
+                    rope: Rope | None = None, out=None, stream=None,
+                    skip_threshold: float = 0.0):
     """FP8 stage 2 (h3_attn_packed_fp8): attention of ``q`` (normalised + rotated in
     registers when ``w_q`` is given) against FP8 tiles packed by ``kv_pack_fp8``."""
     s_in = _row_stride(q, "q")
@@ -335,7 +338,20 @@ def attn_packed_fp8(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: 
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_packed_fp8(_p(q), _p(out), _p(w_q), w_head_stride, float(eps),
                                     ctypes.byref(rope) if rope is not None else None,
-                                    float(softmax_scale), ctypes.byref(call.shape),
-                                    _p(workspace), workspace.numel(), ctypes.c_void_p(st)),
-           "h3_attn_packed_fp8")
+                                    float(softmax_scale), float(skip_threshold),
+                                    ctypes.byref(call.shape), _p(workspace), workspace.numel(),
+                                    ctypes.c_void_p(st)), "h3_attn_packed_fp8")
     return out
+
+
+def fp8_skip_counts(workspace, x: torch.Tensor) -> torch.Tensor:
+    """Skip counts the last FP8 attention call left in ``workspace`` for a tensor shaped
+    like ``x``: [B, H, ceil(S / 256)] int32, wave tiles (32 rows x 64 keys) skipped per
+    256-row workgroup (layout documented with h3_attn_fp8_workspace_size)."""
+    B, S, H, D = _dims(x)
+    tiles = (S + 63) // 64
+    img = B * H * tiles * 19456
+    vamax = (B * H * D * 4 + 255) // 256 * 256
+    blocks = (S + 255) // 256
+    n = B * H * blocks
+    return workspace[img + vamax: img + vamax + 4 * n].view(torch.int32).view(B, H, blocks)

@@ -19,6 +19,12 @@
 //      carried to a new maximum by 2^(m_(t-1) - m_t).  The row sums are the sums of the
 //      quantized P, taken by one extra FP8 product with an all-ones operand.
 //   O = s_v * (P V) / l, rounded to bf16; rows in [N, S) are zero.
+//   Skip-Softmax (same section: tiles judged unimportant from the QK result skip the
+//      softmax and the P V product; a higher threshold skips more): with threshold
+//      lambda, tile t >= 1 is dropped for a row when 2^(tile max - m_(t-1)) < lambda
+//      (scaled scores in log2 units, m_(t-1) the running maximum before the tile); the
+//      row's P for that tile is then 0 and its maximum unchanged.  A wave whose 32 rows
+//      all drop a tile skips that tile's softmax, PV and row-sum products.
 //
 // FP8 tile image (64 keys, 19,456 bytes):
 //   K part: key r, channel c at byte r*144 + c (128 bytes of codes + 16 bytes pad; row
@@ -245,6 +251,8 @@ struct Fp8AttnArgs {
   int64_t w_head_stride;
   float eps;
   RopeArgs rope;
+  float skip_log2;          // log2(Skip-Softmax threshold); -inf: never skip
+  uint32_t* skipped;        // [head * m_tiles]: wave tiles skipped by each workgroup
 };
 
 namespace fp8 {
@@ -261,6 +269,9 @@ struct Wave {
   i32x8 p;           // P codes, B operand (byte b = value b of the tile, see the image)
   float m;           // running max (log2 units)
   float c;           // softmax_scale * log2(e) * sq (this row's Q scale)
+  bool skip;         // this row drops the current tile (Skip-Softmax)
+  bool skip_all;     // every row of the wave drops it (wave-uniform)
+  uint32_t skipped;  // wave tiles skipped so far
 };
 
 }  // namespace fp8
@@ -268,7 +279,7 @@ struct Wave {
 // 8 waves x 32 query rows per workgroup, two waves per SIMD; per 64-key tile and wave:
 // 4 QK products, the softmax of the previous tile, 4 PV products and the row-sum
 // product.  One barrier per tile; tiles are copied global -> LDS into a 3-slot ring.
-template <bool kFusedQ>
+template <bool kFusedQ, bool kSkip>
 __global__ __launch_bounds__(fp8::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fp8_kernel(Fp8AttnArgs a) {
   using namespace fp8;
@@ -283,6 +294,7 @@ attn_fp8_kernel(Fp8AttnArgs a) {
   const int hl = lane >> 5, l32 = lane & 31;
   const int64_t hoff = (int64_t)head * kHeadDim;
   if (m0 >= a.n_valid) {  // rows past the valid length: zeros only
+    if (tid == 0) a.skipped[logical] = 0u;
     const int64_t rows = (a.seq_buf - m0) < kRows ? (a.seq_buf - m0) : kRows;
     for (int64_t i = tid; i < rows * h3::kChunks; i += kThreads) {
       const int64_t r = m0 + i / h3::kChunks;
@@ -349,6 +361,10 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     w.c = a.scale_log2 * (amax / kMax);
   }
   w.m = -INFINITY;
+  w.skip = false;
+  w.skip_all = false;
+  w.skipped = 0u;
+  const bool row_valid = row < a.n_valid;
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
   w.l = f32x16{};
@@ -425,6 +441,10 @@ attn_fp8_kernel(Fp8AttnArgs a) {
         }
       }
     v = pair_max(v);
+    if (kSkip) {  // decided against the maximum before this tile; rows >= N never block
+      w.skip = !row_valid || v < w.m + a.skip_log2;
+      w.skip_all = __builtin_amdgcn_ballot_w64(!w.skip) == 0;
+    }
     const bool need = v > w.m;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float m_new = need ? v : w.m;
@@ -443,7 +463,8 @@ attn_fp8_kernel(Fp8AttnArgs a) {
   auto softmax_half = [&](const f32x16& s, const float* cb, int kb, auto mask_tag)
       __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    const float off = 8.0f - w.m;
+    // a row that drops the tile gets p = exp2(-inf) = 0
+    const float off = (kSkip && w.skip) ? -INFINITY : 8.0f - w.m;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float p[4];
@@ -477,16 +498,19 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     constexpr bool kMaskNext = decltype(mask_next_tag)::value;
     if (j + kSlots - 1 < nt) load(j + kSlots - 1);  // into the slot tile j-1 left
     const char* kb0 = slot(j + 1) + k_lane;
+    // every row of the wave drops tile j: no softmax, PV or row-sum products for it
+    const bool run = !(kSkip && w.skip_all);
+    if (!run) ++w.skipped;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (!kLast) {
         nxt[kb] = fp8::mfma8(read32(kb0 + kb * 32 * kKPitch), w.q[0], f32x16{});
         nxt[kb] = fp8::mfma8(read32(kb0 + kb * 32 * kKPitch + 64), w.q[1], nxt[kb]);
       }
-      softmax_half(cur[kb], cbc, kb, std::integral_constant<bool, kLast>{});
+      if (run) softmax_half(cur[kb], cbc, kb, std::integral_constant<bool, kLast>{});
       __builtin_amdgcn_sched_barrier(0);
     }
-    pv(j);
+    if (run) pv(j);
     if (!kLast) {
       block_c(j + 1, cbn);
       update_max(nxt, cbn, std::integral_constant<bool, kMaskNext>{});
@@ -532,6 +556,20 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     }
     step(sa, sb, ca, cb, nt - 2, F{}, T{});
     step(sb, sa, cb, ca, nt - 1, T{}, F{});
+  }
+
+  if (kSkip) {  // wave tiles this workgroup skipped
+    __shared__ uint32_t wave_skipped[kWaves];
+    if (lane == 0) wave_skipped[wave] = w.skipped;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t total = 0;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) total += wave_skipped[i];
+      a.skipped[logical] = total;
+    }
+  } else if (tid == 0) {
+    a.skipped[logical] = 0u;
   }
 
   // ---- epilogue: lane holds O^T[d = db*32 + 8i + 4hl + j][row] at register 4i+j

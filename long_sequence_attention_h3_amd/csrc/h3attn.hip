@@ -128,15 +128,21 @@ h3_status launched() { return hipGetLastError() == hipSuccess ? H3_OK : H3_ERR_L
   } while (0)
 
 // FP8 workspace: tile images, [batch][head][tile] x fp8::kTileBytes, then the per-channel
-// V maxima, [batch][head][128] floats, rounded up to 256 bytes.
+// V maxima, [batch][head][128] floats, then one skipped-tile count per attention
+// workgroup, [batch][head][ceil(S/256)] uint32; each part rounded up to 256 bytes.
 size_t fp8_batch_img_bytes(const h3_shape* s) {
   return (size_t)s->num_heads * (size_t)tiles_per_head(s) * (size_t)fp8::kTileBytes;
 }
 size_t fp8_vamax_words(const h3_shape* s) {
   return (size_t)s->batch * (size_t)s->num_heads * kHeadDim;
 }
+size_t fp8_vamax_bytes(const h3_shape* s) { return (fp8_vamax_words(s) * 4 + 255) & ~size_t(255); }
+size_t fp8_count_words(const h3_shape* s) {
+  return (size_t)s->batch * (size_t)s->num_heads * (size_t)((s->seq_buf + fp8::kRows - 1) / fp8::kRows);
+}
 size_t fp8_workspace_bytes(const h3_shape* s) {
-  return (size_t)s->batch * fp8_batch_img_bytes(s) + ((fp8_vamax_words(s) * 4 + 255) & ~size_t(255));
+  return (size_t)s->batch * fp8_batch_img_bytes(s) + fp8_vamax_bytes(s) +
+         ((fp8_count_words(s) * 4 + 255) & ~size_t(255));
 }
 
 h3_status check_workspace(const h3_shape* s, const void* ws, size_t bytes, bool is_fp8 = false) {
@@ -305,13 +311,14 @@ h3_status do_kv_pack_fp8(const void* k, const void* v, const void* w_k, int64_t 
 // ---------------------------------------------------------------- FP8 stage 2
 h3_status do_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_head_stride,
                              float eps, const h3_rope* rope, float softmax_scale,
-                             const h3_shape* shp, const void* workspace, size_t ws_bytes,
-                             hipStream_t stream) {
+                             float skip_threshold, const h3_shape* shp, void* workspace,
+                             size_t ws_bytes, hipStream_t stream) {
   int64_t max_valid = 0;
   H3_TRY(check_shape(shp, &max_valid));
   if (!q || !o) return H3_ERR_NULL;
   if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  if (!(skip_threshold >= 0.0f && skip_threshold < 1.0f)) return H3_ERR_SHAPE;
   const bool norm = w_q != nullptr;
   RopeArgs ra{};
   if (norm) H3_TRY(check_norm(w_q, w_head_stride, eps, rope, max_valid, &ra));
@@ -324,8 +331,13 @@ h3_status do_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_
   const size_t per_batch = fp8_batch_img_bytes(shp);
   const uint32_t* vamax = reinterpret_cast<const uint32_t*>(
       static_cast<const char*>(workspace) + shp->batch * per_batch);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                 shp->batch * per_batch + fp8_vamax_bytes(shp));
+  const bool skip = skip_threshold > 0.0f;
   for (int b = 0; b < shp->batch; ++b) {
     Fp8AttnArgs aa{};
+    aa.skip_log2 = skip ? (float)std::log2((double)skip_threshold) : -INFINITY;
+    aa.skipped = counts + (int64_t)b * H * m_tiles;
     aa.q = static_cast<const __bf16*>(q) + b * S * shp->in_row_stride;
     aa.o = static_cast<__bf16*>(o) + b * S * shp->out_row_stride;
     aa.img = static_cast<const char*>(workspace) + b * per_batch;
@@ -343,10 +355,14 @@ h3_status do_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_
     aa.eps = eps;
     aa.rope = ra;
     const unsigned blocks = (unsigned)((int64_t)H * m_tiles);
-    if (norm)
-      attn_fp8_kernel<true><<<blocks, fp8::kThreads, 0, stream>>>(aa);
+    if (norm && skip)
+      attn_fp8_kernel<true, true><<<blocks, fp8::kThreads, 0, stream>>>(aa);
+    else if (norm)
+      attn_fp8_kernel<true, false><<<blocks, fp8::kThreads, 0, stream>>>(aa);
+    else if (skip)
+      attn_fp8_kernel<false, true><<<blocks, fp8::kThreads, 0, stream>>>(aa);
     else
-      attn_fp8_kernel<false><<<blocks, fp8::kThreads, 0, stream>>>(aa);
+      attn_fp8_kernel<false, false><<<blocks, fp8::kThreads, 0, stream>>>(aa);
     H3_TRY(launched());
   }
   return H3_OK;
@@ -475,36 +491,39 @@ h3_status h3_kv_pack_fp8(const void* k, const void* v, const void* w_k, int64_t 
 
 h3_status h3_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_head_stride,
                              float eps, const h3_rope* rope, float softmax_scale,
-                             const h3_shape* shape, const void* workspace,
+                             float skip_threshold, const h3_shape* shape, void* workspace,
                              size_t workspace_bytes_, hipStream_t stream) {
-  return do_attn_packed_fp8(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape,
-                            workspace, workspace_bytes_, stream);
+  return do_attn_packed_fp8(q, o, w_q, w_head_stride, eps, rope, softmax_scale, skip_threshold,
+                            shape, workspace, workspace_bytes_, stream);
 }
 
 h3_status h3_attn_varlen_fp8(const void* q, const void* k, const void* v, void* o,
-                             float softmax_scale, const h3_shape* shape, void* workspace,
-                             size_t workspace_bytes_, hipStream_t stream) {
+                             float softmax_scale, float skip_threshold, const h3_shape* shape,
+                             void* workspace, size_t workspace_bytes_, hipStream_t stream) {
   if (!q || !o) return H3_ERR_NULL;
   if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  if (!(skip_threshold >= 0.0f && skip_threshold < 1.0f)) return H3_ERR_SHAPE;
   H3_TRY(do_kv_pack_fp8(k, v, nullptr, 0, 0.0f, nullptr, shape, workspace, workspace_bytes_,
                         stream));
-  return do_attn_packed_fp8(q, o, nullptr, 0, 0.0f, nullptr, softmax_scale, shape, workspace,
-                            workspace_bytes_, stream);
+  return do_attn_packed_fp8(q, o, nullptr, 0, 0.0f, nullptr, softmax_scale, skip_threshold,
+                            shape, workspace, workspace_bytes_, stream);
 }
 
 h3_status h3_attn_layer_fp8(const void* q, const void* k, const void* v, void* o,
                             const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
-                            const h3_rope* rope, float softmax_scale, const h3_shape* shape,
-                            void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+                            const h3_rope* rope, float softmax_scale, float skip_threshold,
+                            const h3_shape* shape, void* workspace, size_t workspace_bytes_,
+                            hipStream_t stream) {
   if (!q || !o || !w_q || !w_k) return H3_ERR_NULL;
   if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  if (!(skip_threshold >= 0.0f && skip_threshold < 1.0f)) return H3_ERR_SHAPE;
   H3_TRY(check_weights(w_q, w_k, w_head_stride));
   H3_TRY(do_kv_pack_fp8(k, v, w_k, w_head_stride, eps, rope, shape, workspace,
                         workspace_bytes_, stream));
-  return do_attn_packed_fp8(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape,
-                            workspace, workspace_bytes_, stream);
+  return do_attn_packed_fp8(q, o, w_q, w_head_stride, eps, rope, softmax_scale, skip_threshold,
+                            shape, workspace, workspace_bytes_, stream);
 }
 
 }  // extern "C"

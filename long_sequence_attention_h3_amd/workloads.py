@@ -87,15 +87,49 @@ def generate(w: Workload, tail: str | None = "nan", seed: int | None = None,
     for name in ("w_q", "w_k"):
         out[name] = (1.0 + 0.1 * torch.randn((D,), generator=g, dtype=torch.float32)).to(
             torch.bfloat16)
-    fill = tail_fill_bits(tail)
     n_valid = [w.n_valid] * B if n_valid is None else list(n_valid)
     assert len(n_valid) == B and all(0 <= n <= S for n in n_valid)
+    _fill_tail(out, tail, n_valid)
+    out["n_valid"] = n_valid
+    return out
+
+
+def _fill_tail(out: dict, tail: str | None, n_valid: list):
+    fill = tail_fill_bits(tail)
     if fill is not None:
         for name in ("q", "k", "v"):
             bits = out[name].view(torch.int16)
-            for b in range(B):
+            for b in range(len(n_valid)):
                 bits[b, n_valid[b]:] = torch.tensor(fill, dtype=torch.int32).to(torch.int16)
-    out["n_valid"] = n_valid
+
+
+def generate_local(w: Workload, alpha: float = 10.0, frame: int = 804, tail: str | None = "nan",
+                   seed: int | None = None) -> dict:
+    """Seeded inputs with local structure, a stand-in for the peakier score distributions
+    of a trained model: ``generate(w, tail=None, seed)`` (same draws), then one random
+    unit direction per block of ``frame`` consecutive tokens and head is added with
+    weight ``alpha`` to Q and K of every token of the block, rounded to bf16 again; V is
+    unchanged.  The directions (fp32 N(0,1) [ceil(S / frame), H, 32] from a second
+    generator seeded with seed + 1,000,003, normalised) occupy channels 48..63 and
+    112..127 only: the 16 lowest-frequency pairs of the half-split rotary embedding,
+    which turn by less than 1 radian over 804 positions, so the structure survives
+    RoPE.  Tokens then attend mostly within their block (804 = 12 x 67 is one video
+    frame of the long workload's grid).  Tail rows as in ``generate``."""
+    base = w.seed if seed is None else seed
+    out = generate(w, tail=None, seed=base)
+    B, S, H, D = w.batch, w.seq_buf, w.heads, w.head_dim
+    g = torch.Generator(device="cpu")
+    g.manual_seed(base + 1_000_003)
+    nblk = (S + frame - 1) // frame
+    u = torch.randn((nblk, H, 32), generator=g, dtype=torch.float32)
+    u = u / u.norm(dim=-1, keepdim=True)
+    full = torch.zeros((nblk, H, D), dtype=torch.float32)
+    full[:, :, D // 2 - 16:D // 2] = u[:, :, :16]
+    full[:, :, D - 16:] = u[:, :, 16:]
+    per_token = full.repeat_interleave(frame, dim=0)[:S]  # [S, H, D]
+    for name in ("q", "k"):
+        out[name] = (out[name].float() + alpha * per_token).to(torch.bfloat16)
+    _fill_tail(out, tail, out["n_valid"])
     return out
 
 

@@ -162,15 +162,17 @@ def test_fp8_workspace_size_formula():
     L = B.lib()
     tile = 64 * 144 + 128 * 80  # K rows of 128 codes + 16 pad, V rows of 64 codes + 16 pad
 
-    def vamax(words):  # one float per channel, head and batch, rounded up to 256 bytes
-        return (words * 4 + 255) // 256 * 256
+    def words(n):  # n 4-byte words rounded up to 256 bytes
+        return (n * 4 + 255) // 256 * 256
 
     assert tile == 19456
     f = L.h3_attn_fp8_workspace_size
+    # tiles, then one V maximum per channel/head/batch, then one skip count per 256 rows
     assert f(ctypes.byref(shape(H=42, S=58816, valid=(58758,)))) == \
-        42 * 919 * tile + vamax(42 * 128)
-    assert f(ctypes.byref(shape(S=65, valid=(1,)))) == 2 * 2 * tile + vamax(2 * 128)
-    assert f(ctypes.byref(shape(B_=3, S=64, valid=(1, 2, 3)))) == 3 * 2 * tile + vamax(3 * 256)
+        42 * 919 * tile + words(42 * 128) + words(42 * 230)
+    assert f(ctypes.byref(shape(S=65, valid=(1,)))) == 2 * 2 * tile + words(2 * 128) + words(2)
+    assert f(ctypes.byref(shape(B_=3, S=64, valid=(1, 2, 3)))) == \
+        3 * 2 * tile + words(3 * 256) + words(6)
     assert f(ctypes.byref(shape(D=64))) == 0
     assert f(None) == 0
 
@@ -188,21 +190,26 @@ def test_fp8_entry_points_validate():
                             None) == 3
     assert L.h3_kv_pack_fp8(FAKE, FAKE, FAKE, 0, 1e-6, None, ctypes.byref(s), WS, need,
                             None) == 1
-    assert L.h3_attn_packed_fp8(FAKE, 0, None, 0, 0.0, None, 0.1, ctypes.byref(s), WS, need,
+    assert L.h3_attn_packed_fp8(FAKE, 0, None, 0, 0.0, None, 0.1, 0.0, ctypes.byref(s), WS, need,
                                 None) == 1
     assert L.h3_attn_packed_fp8(FAKE, FAKE, FAKE, 0, 1e-6, ctypes.byref(rope(n_1d=10)), 0.1,
-                                ctypes.byref(s), WS, need, None) == 4
-    assert L.h3_attn_packed_fp8(FAKE, FAKE, None, 0, 0.0, None, float("nan"),
+                                0.0, ctypes.byref(s), WS, need, None) == 4
+    assert L.h3_attn_packed_fp8(FAKE, FAKE, None, 0, 0.0, None, float("nan"), 0.0,
                                 ctypes.byref(s), WS, need, None) == 2
-    assert L.h3_attn_varlen_fp8(FAKE, FAKE, FAKE, FAKE, 0.088, ctypes.byref(shape(D=64)), WS,
-                                need, None) == 4
-    assert L.h3_attn_varlen_fp8(FAKE, FAKE, FAKE, FAKE, 0.088, ctypes.byref(s), WS, need - 1,
-                                None) == 7
+    for bad in (-0.1, 1.0, float("nan")):  # Skip-Softmax threshold outside [0, 1)
+        assert L.h3_attn_packed_fp8(FAKE, FAKE, None, 0, 0.0, None, 0.1, bad,
+                                    ctypes.byref(s), WS, need, None) == 2
+        assert L.h3_attn_varlen_fp8(FAKE, FAKE, FAKE, FAKE, 0.088, bad, ctypes.byref(s), WS,
+                                    need, None) == 2
+    assert L.h3_attn_varlen_fp8(FAKE, FAKE, FAKE, FAKE, 0.088, 0.0, ctypes.byref(shape(D=64)),
+                                WS, need, None) == 4
+    assert L.h3_attn_varlen_fp8(FAKE, FAKE, FAKE, FAKE, 0.088, 0.0, ctypes.byref(s), WS,
+                                need - 1, None) == 7
     assert L.h3_attn_layer_fp8(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 0, 1e-6, ctypes.byref(rope()),
-                               0.088, ctypes.byref(s), WS, need, None) == 1
+                               0.088, 0.0, ctypes.byref(s), WS, need, None) == 1
     assert L.h3_attn_layer_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1e-6,
-                               ctypes.byref(rope(n_1d=10)), 0.088, ctypes.byref(s), WS, need,
-                               None) == 4
+                               ctypes.byref(rope(n_1d=10)), 0.088, 0.0, ctypes.byref(s), WS,
+                               need, None) == 4
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
@@ -210,12 +217,12 @@ def test_fp8_valid_call_without_device_fails_loudly():
     L = B.lib()
     s = shape()
     need = L.h3_attn_fp8_workspace_size(ctypes.byref(s))
-    assert L.h3_attn_varlen_fp8(FAKE, FAKE, FAKE, FAKE, 0.088, ctypes.byref(s), WS, need,
+    assert L.h3_attn_varlen_fp8(FAKE, FAKE, FAKE, FAKE, 0.088, 0.0, ctypes.byref(s), WS, need,
                                 None) == 5
     assert L.h3_attn_layer_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1e-6,
-                               ctypes.byref(rope()), 0.088, ctypes.byref(s), WS, need,
+                               ctypes.byref(rope()), 0.088, 0.5, ctypes.byref(s), WS, need,
                                None) == 5
     assert L.h3_kv_pack_fp8(FAKE, FAKE, None, 0, 0.0, None, ctypes.byref(s), WS, need,
                             None) == 5
-    assert L.h3_attn_packed_fp8(FAKE, FAKE, None, 0, 0.0, None, 0.1, ctypes.byref(s), WS,
+    assert L.h3_attn_packed_fp8(FAKE, FAKE, None, 0, 0.0, None, 0.1, 0.0, ctypes.byref(s), WS,
                                 need, None) == 5

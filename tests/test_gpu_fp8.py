@@ -246,3 +246,94 @@ def test_fp8_packed_stages_match_one_call(dev):
                                 rope=gpu_rope(w))
         torch.cuda.synchronize()
         assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
+# ---------------------------------------------------------------- Skip-Softmax
+def local_inputs(cfg, alpha, seed=None):
+    w = W.WORKLOADS[cfg]
+    say(f"[inputs] workload {cfg} {w.name} with frame-local structure, alpha={alpha}")
+    return w, W.generate_local(w, alpha=alpha, seed=seed)
+
+
+def skip_rate(ws, x, n_valid):
+    counts = B.fp8_skip_counts(ws, x)
+    waves = (n_valid + 31) // 32
+    tiles = (n_valid + 63) // 64
+    return int(counts.sum()), int(counts.sum()) / max(1, waves * (tiles - 1) * x.shape[-2])
+
+
+@pytest.mark.parametrize("alpha,lam,entry", [(10.0, 0.01, "varlen"), (8.0, 0.001, "varlen"),
+                                             (12.0, 0.01, "layer")])
+def test_fp8_skip_softmax_matches_oracle(alpha, lam, entry, dev):
+    """Skip-Softmax against the oracle's per-row rule.  alpha = 10, lambda = 0.01 drops
+    about half of the (row, tile) pairs and ~40 % of the wave tiles whole; alpha = 8,
+    lambda = 0.001 drops a fifth of the pairs with rows of one wave disagreeing (P zeroed
+    per row, almost no whole wave tile); on the layer path (RMSNorm shrinks the structure
+    by ~1.3x) alpha = 12 drops ~40 % of the pairs and ~20 % of the wave tiles."""
+    w, inp = local_inputs(1, alpha)
+    d = to_dev(inp, dev)
+    ws = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
+    run = gpu_layer_fp8 if entry == "layer" else gpu_varlen_fp8
+    out = run(w, d, workspace=ws, skip_threshold=lam)
+    skipped, rate = skip_rate(ws, d["q"], w.n_valid)
+    dense = run(w, d, skip_threshold=0.0)
+    say(f"  {entry} lambda={lam}: {skipped} wave tiles skipped ({100 * rate:.1f} %)")
+    assert_tail_zero(out, inp["n_valid"], entry)
+    rows = np.arange(w.n_valid)
+    q, k, v = (W.bits(inp[x][0]) for x in ("q", "k", "v"))
+    if entry == "varlen":
+        ref = O.attn_varlen_fp8(q, k, v, w.n_valid, scale_of(w), rows, skip_threshold=lam)
+    else:
+        ref = O.attn_layer_fp8(q, k, v, w.n_valid, W.bits(inp["w_q"]), W.bits(inp["w_k"]),
+                               w.eps, oracle_rope(w), scale_of(w), rows, skip_threshold=lam)
+    assert_close(rows_of(out, rows), ref, f"{entry}_fp8 skip {lam}")
+    assert not torch.equal(out.view(torch.int16), dense.view(torch.int16)), "nothing dropped"
+    if alpha >= 10.0:
+        assert rate > 0.1, rate  # whole wave tiles were skipped
+
+
+def test_fp8_skip_result_does_not_depend_on_row_grouping(dev):
+    """Each row's result depends on its own scores only: permuting the query rows (which
+    regroups them into waves, changing which wave tiles are skipped whole) permutes the
+    output bit for bit."""
+    w, inp = local_inputs(1, 10.0)
+    d = to_dev(inp, dev)
+    n = w.n_valid
+    out = gpu_varlen_fp8(w, d, skip_threshold=0.01)
+    g = torch.Generator().manual_seed(77)
+    perm = torch.randperm(n, generator=g).to(dev)
+    qp = d["q"].clone()
+    qp[0, :n] = d["q"][0, perm]
+    outp = gpu_varlen_fp8(w, dict(d, q=qp), skip_threshold=0.01)
+    assert torch.equal(outp[0, :n].view(torch.int16), out[0, perm].view(torch.int16))
+
+
+def test_fp8_skip_counts_zero_when_dense_and_threshold_checked(dev):
+    w, inp = local_inputs(0, 10.0)
+    d = to_dev(inp, dev)
+    ws = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
+    gpu_varlen_fp8(w, d, workspace=ws, skip_threshold=0.01)
+    assert skip_rate(ws, d["q"], w.n_valid)[0] > 0
+    gpu_varlen_fp8(w, d, workspace=ws, skip_threshold=0.0)
+    assert skip_rate(ws, d["q"], w.n_valid)[0] == 0
+    for bad in (-0.5, 1.0):
+        with pytest.raises(B.H3Error):
+            B.attn_varlen_fp8(d["q"], d["k"], d["v"], d["n_valid"], scale_of(w),
+                              skip_threshold=bad)
+
+
+def test_fp8_skip_full_length_sampled(dev):
+    """The 6-head share at full length with frame-local structure, lambda = 0.01, on 128
+    sampled rows per head."""
+    w, inp = local_inputs(2, 12.0)
+    d = to_dev(inp, dev)
+    ws = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
+    out = gpu_layer_fp8(w, d, workspace=ws, skip_threshold=0.01)
+    skipped, rate = skip_rate(ws, d["q"], w.n_valid)
+    say(f"  layer_fp8 full length, lambda=0.01: {100 * rate:.1f} % of wave tiles skipped")
+    rows = W.sample_rows(w, 128, 40_002)
+    q, k, v = (W.bits(inp[x][0]) for x in ("q", "k", "v"))
+    ref = O.attn_layer_fp8(q, k, v, w.n_valid, W.bits(inp["w_q"]), W.bits(inp["w_k"]), w.eps,
+                           oracle_rope(w), scale_of(w), np.asarray(rows), skip_threshold=0.01)
+    assert_close(rows_of(out, rows), ref, "layer_fp8 skip full length")
+    assert rate > 0.1, rate
