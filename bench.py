@@ -13,7 +13,10 @@ inputs already resident in HBM.  Prints one JSON line:
   kernels    the other kernels' achieved bandwidth (K/V pre-pass, standalone prologue)
   fp8        the FP8 (SAGE) variant on the same workload: h3_attn_layer_fp8 per step, its
              attention kernel alone (h3_attn_packed_fp8) against the FP8 dense MFMA peak,
-             and its pre-pass; reported beside the bf16 headline, never as `value`
+             and its pre-pass; reported beside the bf16 headline, never as `value`.
+             fp8.skip_softmax: the same step with Skip-Softmax (threshold 0.01) on these
+             inputs and on frame-local inputs of the same shape, with the share of wave
+             tiles skipped and the dense bf16 / dense FP8 times on those inputs
   per_workload  every workload size: h3_attn_layer and h3_attn_varlen TFLOP/s (median and
              min of 10 calls after 3 warm-up calls), the same for the FP8 calls, and
              h3_qk_rmsnorm_rope GB/s
@@ -43,6 +46,8 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s + % bf16 MFMA peak, 42 heads x 58,758 valid tokens, 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense FP8 MFMA, published
+SKIP_LAMBDA = 0.01             # Skip-Softmax threshold reported by the bench
+LOCAL_ALPHA = 12.0             # strength of the frame-local input structure
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = ("long_sequence_attention_h3_amd/csrc/attention.hpp",
                   "long_sequence_attention_h3_amd/csrc/common.hpp",
@@ -336,7 +341,44 @@ def main() -> int:
         f"attn_fp8_kernel {ms_attn8:.3f} ms ({fp8['attention_kernel']['tflops']} TFLOP/s, "
         f"{100 * fp8['attention_kernel']['frac_fp8_peak']:.1f}% of fp8 peak), pre-pass "
         f"{ms_pack8:.3f} ms")
-    del ws8, out8
+
+    # ---- Skip-Softmax on the FP8 layer: these inputs, then frame-local ones
+    wave_tiles = w.heads * ((w.n_valid + 31) // 32) * (tiles - 1)
+
+    def skip_run(dd, lam):
+        ms = timed(lambda: B.attn_layer_fp8(dd["q"], dd["k"], dd["v"], dd["w_q"], dd["w_k"], n,
+                                            w.eps, rope, scale, out=out8, workspace=ws8,
+                                            skip_threshold=lam), args.steps)
+        skipped = int(B.fp8_skip_counts(ws8, dd["q"]).sum())
+        return {"ms_per_step": round(ms, 4), "tflops_equiv": round(flops / ms / 1e9, 2),
+                "wave_tiles_skipped": round(skipped / wave_tiles, 4)}
+
+    skip = {"threshold": SKIP_LAMBDA, "rule": "per row, a 64-key tile after the first is "
+            "dropped when exp(tile max - running max) < threshold",
+            "this_workload": skip_run(d, SKIP_LAMBDA)}
+    t0 = time.time()
+    dl = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+          for k, v in W.generate_local(w, alpha=LOCAL_ALPHA).items()}
+    log(f"[bench] frame-local inputs ready in {time.time() - t0:.1f}s")
+    ms_bf16_local = timed(lambda: B.attn_layer(dl["q"], dl["k"], dl["v"], dl["w_q"], dl["w_k"], n,
+                                               w.eps, rope, scale, out=out, workspace=ws),
+                          args.steps)
+    dense_local = skip_run(dl, 0.0)
+    skip_local = skip_run(dl, SKIP_LAMBDA)
+    skip["frame_local"] = {
+        "inputs": f"workloads.generate_local(alpha={LOCAL_ALPHA}, frame=804): one direction "
+                  "per 804-token block on the 16 lowest-frequency RoPE pairs",
+        "bf16_dense_ms": round(ms_bf16_local, 4), "fp8_dense": dense_local,
+        "fp8_skip": skip_local,
+        "speedup_skip_over_fp8_dense": round(dense_local["ms_per_step"] /
+                                             skip_local["ms_per_step"], 3),
+        "speedup_skip_over_bf16_dense": round(ms_bf16_local / skip_local["ms_per_step"], 3)}
+    fp8["skip_softmax"] = skip
+    log(f"[bench] skip-softmax {SKIP_LAMBDA}: this workload {skip['this_workload']}; "
+        f"frame-local bf16 {ms_bf16_local:.3f} ms, fp8 dense {dense_local['ms_per_step']} ms, "
+        f"fp8 skip {skip_local['ms_per_step']} ms ({100 * skip_local['wave_tiles_skipped']:.1f} % "
+        f"of wave tiles skipped)")
+    del ws8, out8, dl
 
     traffic = measured_traffic()
     result = {

@@ -488,9 +488,9 @@ attn_fp8_kernel(Fp8AttnArgs a) {
 
   // One step for tile j: `cur` holds tile j's scores (its max already applied), `nxt`
   // receives tile j+1's.  Three phases, kept apart with scheduling barriers so that only
-  // one phase's operands are in registers at a time: (A) the QK products of keys 0-31 of
-  // tile j+1 and the P codes of keys 0-31 of tile j; (B) the same for keys 32-63; (C) the
-  // PV and row-sum products of tile j, then the max of tile j+1.  kLast: no tile j+1;
+  // one phase's operands are in registers at a time: (A) channels 0-63 of the QK
+  // products of tile j+1 and the P codes of keys 0-31 of tile j; (B) channels 64-127 and
+  // keys 32-63; (C) the PV and row-sum products of tile j, then the max of tile j+1.  kLast: no tile j+1;
   // kMaskNext: tile j+1 is the last one.
   auto step = [&](f32x16* cur, f32x16* nxt, const float* cbc, float* cbn, int j, auto last_tag,
                   auto mask_next_tag) __attribute__((always_inline)) {
@@ -501,13 +501,15 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     // every row of the wave drops tile j: no softmax, PV or row-sum products for it
     const bool run = !(kSkip && w.skip_all);
     if (!run) ++w.skipped;
+    // phase p: channel half p of the QK products of both key halves of tile j+1 (two
+    // independent products), then the P codes of key half p of tile j
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int p = 0; p < 2; ++p) {
       if (!kLast) {
-        nxt[kb] = fp8::mfma8(read32(kb0 + kb * 32 * kKPitch), w.q[0], f32x16{});
-        nxt[kb] = fp8::mfma8(read32(kb0 + kb * 32 * kKPitch + 64), w.q[1], nxt[kb]);
+        nxt[0] = fp8::mfma8(read32(kb0 + 64 * p), w.q[p], p ? nxt[0] : f32x16{});
+        nxt[1] = fp8::mfma8(read32(kb0 + 32 * kKPitch + 64 * p), w.q[p], p ? nxt[1] : f32x16{});
       }
-      if (run) softmax_half(cur[kb], cbc, kb, std::integral_constant<bool, kLast>{});
+      if (run) softmax_half(cur[p], cbc, p, std::integral_constant<bool, kLast>{});
       __builtin_amdgcn_sched_barrier(0);
     }
     if (run) pv(j);
