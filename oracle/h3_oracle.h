@@ -141,6 +141,17 @@ int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        double skip_threshold, const int64_t* rows, int64_t n_rows, int threads,
                        double* out);
 
+/* ---- DiT block steps around attention: see h3_oracle_block.cpp for the reading. */
+
+/* One sequence of seq_buf rows of `hidden` channels: for rows t < n_valid,
+ * x_out = x + gate * a (a bf16 bits; a NULL: x; gate NULL: 1), y = LayerNorm(x_out)
+ * * (1 + scale) + shift (population variance, eps inside the square root); rows
+ * t >= n_valid: x_out = x, y = 0.  fp64 throughout. */
+int h3o_residual_norm_modulate(const float* x, const uint16_t* a, const float* gate,
+                               const float* shift, const float* scale, int64_t seq_buf,
+                               int64_t n_valid, int64_t hidden, double eps, double* x_out,
+                               double* y_out);
+
 #ifdef __cplusplus
 }
 #endif

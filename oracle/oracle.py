@@ -16,7 +16,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "h3_oracle.cpp"), os.path.join(_HERE, "h3_oracle_fp8.cpp")]
+_SRCS = [os.path.join(_HERE, "h3_oracle.cpp"), os.path.join(_HERE, "h3_oracle_fp8.cpp"),
+         os.path.join(_HERE, "h3_oracle_block.cpp")]
 _LIB = os.path.join(_HERE, "libh3oracle.so")
 
 # Plain -O3 (vectorises the independent per-key / per-channel loops); no
@@ -97,6 +98,8 @@ def lib():
         _lib.h3o_attn_layer_fp8.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, I64, D,
                                             ctypes.POINTER(Rope), D, I64, D, P, I64, I, P]
         _lib.h3o_attn_layer_fp8.restype = I
+        _lib.h3o_residual_norm_modulate.argtypes = [P, P, P, P, P, I64, I64, I64, D, P, P]
+        _lib.h3o_residual_norm_modulate.restype = I
     return _lib
 
 
@@ -278,3 +281,23 @@ def attn_layer_fp8(q_bits, k_bits, v_bits, n_valid: int, wq_bits, wk_bits, eps: 
                                     rows.size, threads or default_threads(), _ptr(out)),
            "attn_layer_fp8")
     return out
+
+
+def residual_norm_modulate(x, a_bits, gate, shift, scale, n_valid: int, eps: float):
+    """Gated residual update, LayerNorm and modulation of one sequence in fp64.
+    x: fp32 [S, C]; a_bits: bf16 bits [S, C] or None; gate (or None), shift, scale:
+    fp32 [C].  Returns (x_out, y) as float64 [S, C]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    S, C = x.shape
+    a = None if a_bits is None else _u16(a_bits)
+    g = None if gate is None else np.ascontiguousarray(gate, dtype=np.float32)
+    sh = np.ascontiguousarray(shift, dtype=np.float32)
+    sc = np.ascontiguousarray(scale, dtype=np.float32)
+    x_out = np.empty((S, C), dtype=np.float64)
+    y = np.empty((S, C), dtype=np.float64)
+    _check(lib().h3o_residual_norm_modulate(_ptr(x), _ptr(a) if a is not None else None,
+                                            _ptr(g) if g is not None else None, _ptr(sh),
+                                            _ptr(sc), S, int(n_valid), C, float(eps),
+                                            _ptr(x_out), _ptr(y)),
+           "residual_norm_modulate")
+    return x_out, y
