@@ -10,7 +10,8 @@ inputs already resident in HBM.  Prints one JSON line:
              events on the launch stream) against the bf16 dense MFMA peak
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload
              (sampled query rows of every head), whose rows also gate parity
-  kernels    the other kernels' achieved bandwidth (K/V pre-pass, standalone prologue)
+  kernels    the other kernels' achieved bandwidth (K/V pre-pass, standalone prologue, the
+             fused residual + LayerNorm + modulation steps around attention)
   fp8        the FP8 (SAGE) variant on the same workload: h3_attn_layer_fp8 per step, its
              attention kernel alone (h3_attn_packed_fp8) against the FP8 dense MFMA peak,
              and its pre-pass; reported beside the bf16 headline, never as `value`.
@@ -380,6 +381,24 @@ def main() -> int:
         f"of wave tiles skipped)")
     del ws8, out8, dl
 
+    # ---- DiT block steps around attention: gated residual + LayerNorm + modulation on the
+    # fp32 residual stream [N, 5,376] (after attention) and LayerNorm + modulation alone
+    # (before it); HBM-bound
+    blk_in = W.generate_block(w.seq_buf, w.n_valid, hidden=w.heads * w.head_dim, seed=11)
+    bx = blk_in["x"].to(dev)
+    ba = blk_in["a"].to(dev)
+    bg, bsh, bsc = (blk_in[k].to(dev) for k in ("gate", "shift", "scale"))
+    by = torch.empty(bx.shape, dtype=torch.bfloat16, device=dev)
+    hid = w.heads * w.head_dim
+    ms_blk = timed(lambda: B.residual_norm_modulate(bx, bsh, bsc, n, 1e-6, a=ba, gate=bg, y=by),
+                   args.steps)
+    ms_blk0 = timed(lambda: B.residual_norm_modulate(bx, bsh, bsc, n, 1e-6, y=by), args.steps)
+    blk_bytes = w.n_valid * hid * (4 + 2 + 4 + 2) + (w.seq_buf - w.n_valid) * hid * 2
+    blk0_bytes = w.n_valid * hid * (4 + 2) + (w.seq_buf - w.n_valid) * hid * 2
+    log(f"[bench] residual_norm_modulate gated {ms_blk:.3f} ms ({blk_bytes / ms_blk / 1e6:.0f} "
+        f"GB/s), norm+modulate {ms_blk0:.3f} ms ({blk0_bytes / ms_blk0 / 1e6:.0f} GB/s)")
+    del bx, ba, bg, bsh, bsc, by, blk_in
+
     traffic = measured_traffic()
     result = {
         "metric": METRIC,
@@ -413,6 +432,14 @@ def main() -> int:
                                     "GB/s": round(prol_bytes / ms_prol / 1e6, 1),
                                     "frac_hbm": round(prol_bytes / ms_prol / 1e6 /
                                                       PEAK_HBM_GBS, 4)},
+            "residual_norm_modulate_kernel (gated residual, after attention)": {
+                "ms": round(ms_blk, 4), "bytes": blk_bytes,
+                "GB/s": round(blk_bytes / ms_blk / 1e6, 1),
+                "frac_hbm": round(blk_bytes / ms_blk / 1e6 / PEAK_HBM_GBS, 4)},
+            "residual_norm_modulate_kernel (norm + modulation, before attention)": {
+                "ms": round(ms_blk0, 4), "bytes": blk0_bytes,
+                "GB/s": round(blk0_bytes / ms_blk0 / 1e6, 1),
+                "frac_hbm": round(blk0_bytes / ms_blk0 / 1e6 / PEAK_HBM_GBS, 4)},
         },
         "fp8": fp8,
         "wall_s_timed_region": round(wall, 4),

@@ -10,7 +10,8 @@
  *           (58,758 valid tokens of 58,816); attention receives the valid length and
  *           the structural tail padding is dropped; RoPE rows are built per token;
  *           heads are 128-channel projections of a 5,376-channel hidden state;
- *     §3.2  "融合的 DiT 算子": Q/K RMSNorm and RoPE are one fused operator;
+ *     §3.2  "融合的 DiT 算子": Q/K RMSNorm and RoPE are one fused operator; the FP32
+ *           modulation, normalization and residual steps are merged into one;
  *     §3.5  speed-ups are "lossless" but not bitwise identical to other kernels;
  *     §4.3  (figure 6) SAGE attention: Q, K, P and V quantized to FP8 for both
  *           attention products; the measured configuration is called "K16".
@@ -226,6 +227,37 @@ h3_status h3_attn_layer_fp8(const void* q, const void* k, const void* v, void* o
                             const h3_rope* rope, float softmax_scale, float skip_threshold,
                             const h3_shape* shape, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * DiT block steps around the attention ([Blog §3.2]: the FP32 modulation,
+ * normalization and residual computations are merged into one operation).  The pages
+ * give no formula; this is the plain adaLN form of a DiT block. */
+
+/* Rows of one or more sequences: x, a and y are [B, S, hidden], contiguous. */
+typedef struct {
+  int32_t batch;             /* B >= 1                                              */
+  int64_t seq_buf;           /* S: rows allocated per sequence                      */
+  const int64_t* seq_valid;  /* HOST array [B]: N_b, 0 <= N_b <= S                  */
+  int64_t hidden;            /* channels per row: a multiple of 8, at most 8,192    */
+} h3_rows;
+
+/* For every valid row t < N_b of batch b, over its `hidden` channels c:
+ *   if a != NULL:  x[c] <- x[c] + gate[c] * a[c]   (fp32 fused multiply-add; gate NULL:
+ *                  gate 1), written back into x
+ *   y[c] = bf16( (x[c] - mean) / sqrt(var + eps) * (1 + scale[c]) + shift[c] )
+ * with mean and var the mean and population variance of the row's x (after the
+ * update), in fp32.  Rows [N_b, S): y written as +0, x neither read nor written.
+ * x: fp32 device [B, S, hidden], read (and updated when a != NULL).  a: bf16 device
+ * [B, S, hidden] (e.g. the attention output after its projection) or NULL.  gate,
+ * shift, scale: fp32 device vectors of batch b at base + b * mod_batch_stride
+ * (mod_batch_stride 0: shared by all batches, else >= hidden and a multiple of 4).
+ * y: bf16 device [B, S, hidden]; must not overlap x or a.  All pointers 16-byte aligned.
+ * Errors: H3_ERR_NULL, H3_ERR_SHAPE, H3_ERR_ALIGN, H3_ERR_UNSUPPORTED (hidden not a
+ * multiple of 8 or above 8,192), H3_ERR_DEVICE, H3_ERR_LAUNCH. */
+h3_status h3_residual_norm_modulate(void* x, const void* a, const float* gate,
+                                    const float* shift, const float* scale,
+                                    int64_t mod_batch_stride, float eps, void* y,
+                                    const h3_rows* rows, hipStream_t stream);
 
 #ifdef __cplusplus
 }

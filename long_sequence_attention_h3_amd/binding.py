@@ -42,6 +42,12 @@ class Rope(ctypes.Structure):
                 ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32)]
 
 
+class Rows(ctypes.Structure):
+    """``h3_rows``."""
+    _fields_ = [("batch", ctypes.c_int32), ("seq_buf", ctypes.c_int64),
+                ("seq_valid", ctypes.POINTER(ctypes.c_int64)), ("hidden", ctypes.c_int64)]
+
+
 def make_rope(theta: float, n_1d: int, sections=(0, 0, 0), grid=(0, 0, 0)) -> Rope:
     r = Rope()
     r.theta = float(theta)
@@ -55,7 +61,7 @@ def make_rope(theta: float, n_1d: int, sections=(0, 0, 0), grid=(0, 0, 0)) -> Ro
 EXPORTED = ("h3_status_string", "h3_version", "h3_qk_rmsnorm_rope", "h3_attn_workspace_size",
             "h3_kv_pack", "h3_attn_packed", "h3_attn_varlen", "h3_attn_layer",
             "h3_attn_fp8_workspace_size", "h3_kv_pack_fp8", "h3_attn_packed_fp8",
-            "h3_attn_varlen_fp8", "h3_attn_layer_fp8")
+            "h3_attn_varlen_fp8", "h3_attn_layer_fp8", "h3_residual_norm_modulate")
 
 _lib = None
 
@@ -97,6 +103,9 @@ def lib():
         L.h3_attn_varlen_fp8.restype = ctypes.c_int
         L.h3_attn_layer_fp8.argtypes = [P, P, P, P, P, P, I64, F, RP, F, F, SH, P, SZ, P]
         L.h3_attn_layer_fp8.restype = ctypes.c_int
+        L.h3_residual_norm_modulate.argtypes = [P, P, P, P, P, I64, F, P,
+                                                ctypes.POINTER(Rows), P]
+        L.h3_residual_norm_modulate.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -355,3 +364,37 @@ def fp8_skip_counts(workspace, x: torch.Tensor) -> torch.Tensor:
     blocks = (S + 255) // 256
     n = B * H * blocks
     return workspace[img + vamax: img + vamax + 4 * n].view(torch.int32).view(B, H, blocks)
+
+
+def residual_norm_modulate(x, shift, scale, n_valid, eps: float = 1e-6, a=None, gate=None,
+                           y=None, stream=None):
+    """DiT block steps around attention (h3_residual_norm_modulate): with ``a``, the fp32
+    residual stream ``x`` is updated in place to x + gate * a; then
+    y = LayerNorm(x) * (1 + scale) + shift in bf16 is returned.  x: fp32 [B, S, C] or
+    [S, C]; a: bf16 of the same shape or None; gate (or None), shift, scale: fp32 [C]
+    (shared) or [B, C]."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 device tensor")
+    xb = x if x.dim() == 3 else x.unsqueeze(0)
+    B, S, C = xb.shape
+    if a is not None and (a.dtype != torch.bfloat16 or a.shape != x.shape or
+                          not a.is_contiguous()):
+        raise ValueError("a must be a contiguous bf16 tensor shaped like x")
+    vecs = [t for t in (gate, shift, scale) if t is not None]
+    for t in vecs:
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.shape[-1] != C:
+            raise ValueError("gate, shift and scale must be contiguous fp32 [..., C]")
+    mod_stride = 0 if shift.dim() == 1 else C
+    for t in vecs:
+        if (0 if t.dim() == 1 else C) != mod_stride:
+            raise ValueError("gate, shift and scale must all be [C] or all [B, C]")
+    y = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device) if y is None else y
+    if isinstance(n_valid, int):
+        n_valid = [n_valid] * B
+    valid = (ctypes.c_int64 * B)(*[int(n) for n in n_valid])
+    rows = Rows(B, S, ctypes.cast(valid, ctypes.POINTER(ctypes.c_int64)), C)
+    st = _stream(x.device) if stream is None else stream
+    _check(lib().h3_residual_norm_modulate(_p(x), _p(a), _p(gate), _p(shift), _p(scale),
+                                           mod_stride, float(eps), _p(y), ctypes.byref(rows),
+                                           ctypes.c_void_p(st)), "h3_residual_norm_modulate")
+    return y

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh3attn.so")
 SOURCES = [os.path.join(CSRC, "h3attn.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("common.hpp", "prologue.hpp", "attention.hpp",
-                                                "attention_fp8.hpp")] + [
+                                                "attention_fp8.hpp", "block.hpp")] + [
     os.path.join(ROOT, "include", "h3attn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

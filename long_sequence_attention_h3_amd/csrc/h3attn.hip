@@ -1,11 +1,12 @@
 // h3attn.hip — libh3attn: C ABI entry points (declared in include/h3attn.h), argument
-// validation and kernel launches.  Kernels live in prologue.hpp, attention.hpp and
-// attention_fp8.hpp.
+// validation and kernel launches.  Kernels live in prologue.hpp, attention.hpp,
+// attention_fp8.hpp and block.hpp.
 //
 // Pages: "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH3 的实时服务"
 // (Chinese translation of the vLLM blog post), §3.1 (valid-length attention over an
-// aligned packed buffer, per-token RoPE rows), §3.2 (fused Q/K RMSNorm + RoPE) and §4.3
-// (the FP8 "SAGE" variant of the attention).
+// aligned packed buffer, per-token RoPE rows), §3.2 (fused Q/K RMSNorm + RoPE; the merged
+// FP32 modulation, normalization and residual steps) and §4.3 (the FP8 "SAGE" variant of
+// the attention and Skip-Softmax).
 #include "h3attn.h"
 
 #include <hip/hip_runtime.h>
@@ -16,6 +17,7 @@
 
 #include "attention.hpp"
 #include "attention_fp8.hpp"
+#include "block.hpp"
 #include "prologue.hpp"
 
 namespace {
@@ -524,6 +526,49 @@ h3_status h3_attn_layer_fp8(const void* q, const void* k, const void* v, void* o
                         workspace_bytes_, stream));
   return do_attn_packed_fp8(q, o, w_q, w_head_stride, eps, rope, softmax_scale, skip_threshold,
                             shape, workspace, workspace_bytes_, stream);
+}
+
+h3_status h3_residual_norm_modulate(void* x, const void* a, const float* gate,
+                                    const float* shift, const float* scale,
+                                    int64_t mod_batch_stride, float eps, void* y,
+                                    const h3_rows* rows, hipStream_t stream) {
+  if (!rows || !rows->seq_valid || !x || !y || !shift || !scale) return H3_ERR_NULL;
+  if (rows->batch < 1 || rows->seq_buf < 0 || rows->hidden < 8) return H3_ERR_SHAPE;
+  if ((rows->hidden % 8) != 0 || rows->hidden > 8 * blk::kThreads * blk::kMaxChunks)
+    return H3_ERR_UNSUPPORTED;
+  if (rows->seq_buf > ((int64_t)1 << 31) - 1) return H3_ERR_SHAPE;
+  if (mod_batch_stride != 0 && mod_batch_stride < rows->hidden) return H3_ERR_SHAPE;
+  if ((mod_batch_stride % 4) != 0) return H3_ERR_ALIGN;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return H3_ERR_SHAPE;
+  for (int b = 0; b < rows->batch; ++b)
+    if (rows->seq_valid[b] < 0 || rows->seq_valid[b] > rows->seq_buf) return H3_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(shift) || !aligned16(scale) ||
+      (a && !aligned16(a)) || (gate && !aligned16(gate)))
+    return H3_ERR_ALIGN;
+  H3_TRY(check_device());
+  const int64_t S = rows->seq_buf, C = rows->hidden;
+  if (S == 0) return H3_OK;
+  for (int b = 0; b < rows->batch; ++b) {
+    BlockArgs ba{};
+    ba.x = static_cast<float*>(x) + b * S * C;
+    ba.a = a ? static_cast<const __bf16*>(a) + b * S * C : nullptr;
+    ba.gate = gate ? gate + b * mod_batch_stride : nullptr;
+    ba.shift = shift + b * mod_batch_stride;
+    ba.scale = scale + b * mod_batch_stride;
+    ba.y = static_cast<__bf16*>(y) + b * S * C;
+    ba.hidden = C;
+    ba.n_valid = rows->seq_valid[b];
+    ba.eps = eps;
+    const unsigned grid = (unsigned)S;
+    if (a && gate)
+      residual_norm_modulate_kernel<true, true><<<grid, blk::kThreads, 0, stream>>>(ba);
+    else if (a)
+      residual_norm_modulate_kernel<true, false><<<grid, blk::kThreads, 0, stream>>>(ba);
+    else
+      residual_norm_modulate_kernel<false, false><<<grid, blk::kThreads, 0, stream>>>(ba);
+    H3_TRY(launched());
+  }
+  return H3_OK;
 }
 
 }  // extern "C"

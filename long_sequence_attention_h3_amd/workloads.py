@@ -133,6 +133,32 @@ def generate_local(w: Workload, alpha: float = 10.0, frame: int = 804, tail: str
     return out
 
 
+def generate_block(seq_buf: int, n_valid, hidden: int = 5376, batch: int = 1, seed: int = 0,
+                   tail: str | None = "nan", per_batch_mod: bool = False) -> dict:
+    """Seeded inputs of the block steps around attention: the fp32 residual stream
+    x = 0.5 + 2 N(0,1) [B, S, hidden], the branch output a = bf16(N(0,1)) of the same
+    shape, then gate, shift and scale = 0.2 N(0,1) fp32 ([hidden], or [B, hidden] with
+    ``per_batch_mod``), drawn in that order from one generator; rows [N_b, S) of x and a
+    are overwritten with ``tail`` (x takes the fp32 pattern of the same value)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    B, S, C = batch, seq_buf, hidden
+    out = {"x": 0.5 + 2.0 * torch.randn((B, S, C), generator=g, dtype=torch.float32),
+           "a": torch.randn((B, S, C), generator=g, dtype=torch.float32).to(torch.bfloat16)}
+    shape = (B, C) if per_batch_mod else (C,)
+    for name in ("gate", "shift", "scale"):
+        out[name] = 0.2 * torch.randn(shape, generator=g, dtype=torch.float32)
+    n_valid = [n_valid] * B if isinstance(n_valid, int) else list(n_valid)
+    assert len(n_valid) == B and all(0 <= n <= S for n in n_valid)
+    fill = {"nan": float("nan"), "big": 3.0e4, "zero": 0.0, None: None}[tail]
+    if fill is not None:
+        for b in range(B):
+            out["x"][b, n_valid[b]:] = fill
+            out["a"][b, n_valid[b]:] = fill
+    out["n_valid"] = n_valid
+    return out
+
+
 def bits(t: torch.Tensor):
     """Bit patterns of a CPU bf16 tensor as a numpy uint16 array (no copy of values)."""
     return t.contiguous().view(torch.int16).numpy().view("uint16")

@@ -226,3 +226,47 @@ def test_fp8_valid_call_without_device_fails_loudly():
                             None) == 5
     assert L.h3_attn_packed_fp8(FAKE, FAKE, None, 0, 0.0, None, 0.1, 0.0, ctypes.byref(s), WS,
                                 need, None) == 5
+
+
+def rows_shape(B_=1, S=64, valid=(60,), C=128):
+    arr = (ctypes.c_int64 * len(valid))(*valid)
+    r = B.Rows(B_, S, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)), C)
+    r._keep = arr
+    return r
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(C=12), 4),          # hidden not a multiple of 8
+    (dict(C=8200), 4),        # hidden above 8,192
+    (dict(C=0), 2),
+    (dict(valid=(65,)), 2),   # N > S
+    (dict(valid=(-1,)), 2),
+    (dict(B_=0), 2),
+])
+def test_block_shape_validation(kwargs, code):
+    L = B.lib()
+    r = rows_shape(**kwargs)
+    assert L.h3_residual_norm_modulate(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1e-6, FAKE,
+                                       ctypes.byref(r), None) == code
+
+
+def test_block_pointer_validation():
+    L = B.lib()
+    r = rows_shape()
+    f = L.h3_residual_norm_modulate
+    assert f(0, FAKE, FAKE, FAKE, FAKE, 0, 1e-6, FAKE, ctypes.byref(r), None) == 1
+    assert f(FAKE, FAKE, FAKE, 0, FAKE, 0, 1e-6, FAKE, ctypes.byref(r), None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1e-6, FAKE, None, None) == 1
+    assert f(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 0, 1e-6, FAKE, ctypes.byref(r), None) == 3
+    assert f(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 0, 1e-6, FAKE, ctypes.byref(r), None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 1e-6, FAKE, ctypes.byref(r), None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 130, 1e-6, FAKE, ctypes.byref(r), None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, -1.0, FAKE, ctypes.byref(r), None) == 2
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present")
+def test_block_valid_call_without_device_fails_loudly():
+    r = rows_shape()
+    assert B.lib().h3_residual_norm_modulate(FAKE, None, None, FAKE, FAKE, 0, 1e-6, FAKE,
+                                             ctypes.byref(r), None) == 5
+
