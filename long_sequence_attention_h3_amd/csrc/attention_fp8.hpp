@@ -376,35 +376,45 @@ attn_fp8_kernel(Fp8AttnArgs a) {
   const char* img = a.img + (int64_t)head * a.tiles_per_head * kTileBytes;
   const int tail = (int)(a.n_valid - (int64_t)(nt - 1) * kTileKeys);
 
-  auto slot = [&](int t) __attribute__((always_inline)) { return smem + (t % kSlots) * kTileBytes; };
+  // LDS byte address of tile t's slot, kept on the scalar unit; operand reads add one
+  // per-lane offset to it and fold their constant offsets into the read instruction
+  typedef __attribute__((address_space(3))) const char lds_char;
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  auto slot_addr = [&](int t) __attribute__((always_inline)) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(smem_addr + ((unsigned)t % (unsigned)kSlots) * (unsigned)kTileBytes));
+  };
+  auto slot = [&](int t) __attribute__((always_inline)) {
+    return smem + ((unsigned)t % (unsigned)kSlots) * (unsigned)kTileBytes;
+  };
   auto load = [&](int t) __attribute__((always_inline)) {
     const char* src = img + (int64_t)t * kTileBytes;
-    char* dst = slot(t);
+    const uint32_t dst = slot_addr(t);
 #pragma unroll
     for (int i = 0; i < (kImgChunks + kWaves - 1) / kWaves; ++i) {
       const int c = wave + i * kWaves;
-      if (c < kImgChunks)
-        dma_to_lds16(src + c * 1024 + lane * 16,
-                     (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(dst + c * 1024));
+      if (c < kImgChunks) dma_to_lds16(src + c * 1024 + lane * 16, dst + c * 1024);
     }
   };
   auto loads_done = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };
-  // per-lane operand bases within a slot
-  const int k_lane = l32 * kKPitch + 32 * hl;
-  const int v_lane = kKBytes + l32 * kVPitch + 32 * hl;
-  auto read32 = [&](const char* p) __attribute__((always_inline)) {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+  // per-lane operand offsets within a slot
+  const uint32_t k_lane = l32 * kKPitch + 32 * hl;
+  const uint32_t v_lane = kKBytes + l32 * kVPitch + 32 * hl;
+  // 32 bytes at LDS address base + off (off a compile-time constant after unrolling)
+  auto read32 = [&](uint32_t base, int off) __attribute__((always_inline)) {
+    lds_char* p = (lds_char*)(uintptr_t)base + off;
+    const u32x4 lo = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(p);
+    const u32x4 hi = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(p + 16);
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   // S^T of tile t: s[kb] (32 keys x 32 rows), register 4i+j = key kb*32 + 8i + 4hl + j
   auto qk = [&](f32x16* s, int t) __attribute__((always_inline)) {
-    const char* kb0 = slot(t) + k_lane;
+    const uint32_t kb0 = slot_addr(t) + k_lane;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = fp8::mfma8(read32(kb0 + kb * 32 * kKPitch), w.q[0], f32x16{});
-      s[kb] = fp8::mfma8(read32(kb0 + kb * 32 * kKPitch + 64), w.q[1], s[kb]);
+      s[kb] = fp8::mfma8(read32(kb0, kb * 32 * kKPitch), w.q[0], f32x16{});
+      s[kb] = fp8::mfma8(read32(kb0, kb * 32 * kKPitch + 64), w.q[1], s[kb]);
     }
   };
   // per-register multipliers c * sk(block): registers 0-7 of half kb are block 2kb,
@@ -480,9 +490,9 @@ attn_fp8_kernel(Fp8AttnArgs a) {
 
   // O^T += V^T P^T and the row sums l += 1^T P^T (exact sums of the quantized weights)
   auto pv = [&](int t) __attribute__((always_inline)) {
-    const char* vb = slot(t) + v_lane;
+    const uint32_t vb = slot_addr(t) + v_lane;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) w.o[db] = fp8::mfma8(read32(vb + db * 32 * kVPitch), w.p, w.o[db]);
+    for (int db = 0; db < 4; ++db) w.o[db] = fp8::mfma8(read32(vb, db * 32 * kVPitch), w.p, w.o[db]);
     w.l = fp8::mfma8(ones, w.p, w.l);
   };
 
@@ -497,7 +507,7 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     constexpr bool kLast = decltype(last_tag)::value;
     constexpr bool kMaskNext = decltype(mask_next_tag)::value;
     if (j + kSlots - 1 < nt) load(j + kSlots - 1);  // into the slot tile j-1 left
-    const char* kb0 = slot(j + 1) + k_lane;
+    const uint32_t kb0 = slot_addr(j + 1) + k_lane;
     // every row of the wave drops tile j: no softmax, PV or row-sum products for it
     const bool run = !(kSkip && w.skip_all);
     if (!run) ++w.skipped;
@@ -506,8 +516,8 @@ attn_fp8_kernel(Fp8AttnArgs a) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       if (!kLast) {
-        nxt[0] = fp8::mfma8(read32(kb0 + 64 * p), w.q[p], p ? nxt[0] : f32x16{});
-        nxt[1] = fp8::mfma8(read32(kb0 + 32 * kKPitch + 64 * p), w.q[p], p ? nxt[1] : f32x16{});
+        nxt[0] = fp8::mfma8(read32(kb0, 64 * p), w.q[p], p ? nxt[0] : f32x16{});
+        nxt[1] = fp8::mfma8(read32(kb0, 32 * kKPitch + 64 * p), w.q[p], p ? nxt[1] : f32x16{});
       }
       if (run) softmax_half(cur[p], cbc, p, std::integral_constant<bool, kLast>{});
       __builtin_amdgcn_sched_barrier(0);
@@ -521,9 +531,9 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     __syncthreads();
   };
 
-  // ---- fill, then one step per tile
   using T = std::true_type;
   using F = std::false_type;
+  // ---- fill, then one step per tile
 #pragma unroll
   for (int t = 0; t < kSlots - 1; ++t)
     if (t < nt) load(t);
