@@ -127,11 +127,14 @@ void h3o_quantize_group(const float* x, int64_t n, double* codes, double* scale)
  * (same layouts and row semantics as h3o_attn_varlen); the weights P are quantized
  * against the running row maximum of tiles of p_tile keys; with skip_threshold > 0 a
  * tile whose maximum is below the running maximum by a factor under skip_threshold
- * is dropped for that row (Skip-Softmax). */
+ * is dropped for that row (Skip-Softmax).  allow (optional, shaped like out): per element,
+ * the largest change of the output that P codes lying within the matrix cores' score
+ * error of a rounding midpoint can cause (see h3_oracle_fp8.cpp). */
 int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int64_t seq_buf, int64_t n_valid, int64_t heads, int64_t d,
                         int64_t row_stride, double scale, int64_t p_tile, double skip_threshold,
-                        const int64_t* rows, int64_t n_rows, int threads, double* out);
+                        const int64_t* rows, int64_t n_rows, int threads, double* out,
+                        double* allow);
 
 /* The FP8 layer: prologue of Q and K (fp64, rounded to bf16), then h3o_attn_varlen_fp8. */
 int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_buf,
@@ -139,7 +142,7 @@ int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        const uint16_t* w_q, const uint16_t* w_k, int64_t w_head_stride,
                        double eps, const h3o_rope* rope, double scale, int64_t p_tile,
                        double skip_threshold, const int64_t* rows, int64_t n_rows, int threads,
-                       double* out);
+                       double* out, double* allow);
 
 /* ---- DiT block steps around attention: see h3_oracle_block.cpp for the reading. */
 

@@ -101,3 +101,25 @@ def assert_tail_zero(out: torch.Tensor, n_valid, label: str):
         if tail.numel():
             bits = tail.contiguous().view(torch.int16)
             assert int(torch.count_nonzero(bits)) == 0, f"{label}: tail rows not +0 (batch {b})"
+
+
+def assert_close_allow(got: np.ndarray, ref: np.ndarray, allow: np.ndarray, label: str):
+    """FP8 bars.  The mean and relative-L2 bars apply to the differences themselves; the
+    max bar applies to the part of each difference beyond the oracle's allowance (P codes
+    within the matrix cores' score error of an E4M3 rounding midpoint may come out one
+    step apart, and the allowance is the most such codes can move each element).  Flips
+    are rare and of either sign, so they leave the mean and L2 at bf16 level; a
+    systematic error cannot hide in the allowance."""
+    assert got.shape == ref.shape == allow.shape
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    d = np.abs(got - ref)
+    raw_mx = float(d.max()) if d.size else 0.0
+    mean = float(d.mean()) if d.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    eff = float(np.maximum(d - allow, 0.0).max()) if d.size else 0.0
+    say(f"  {label}: max|d|={raw_mx:.3e} (beyond allowance {eff:.3e}) mean|d|={mean:.3e} "
+        f"relL2={rel:.3e} over {got.size} values")
+    assert eff <= MAX_ABS, f"{label}: max|d| beyond allowance {eff:.3e} > {MAX_ABS}"
+    assert mean <= MEAN_ABS, f"{label}: mean|d| {mean:.3e} > {MEAN_ABS}"
+    assert rel <= REL_L2, f"{label}: rel-L2 {rel:.3e} > {REL_L2}"
+    return eff, mean, rel

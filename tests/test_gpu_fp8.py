@@ -7,10 +7,14 @@ Page: "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH
   and the per-channel V maxima) are compared bit for bit with the oracle's quantizer
   (codes decoded from the OCP E4M3 definition, scales as fp32 amax / 448).
 - Outputs are compared with the oracle's FP8 attention (P quantized against the running
-  maximum of 64-key tiles) to the layer's bf16 bar: max |delta| <= 1.5e-2, mean |delta|
-  <= 2e-3, relative L2 <= 1e-2.  Both sides quantize Q, K and V to the same codes; the
-  scores differ only by fp32 rounding (about 1e-6 relative), which moves a P code by
-  one E4M3 step on a small fraction of keys, and the output is rounded to bf16.
+  maximum of 64-key tiles, its argument formed in fp32 as the kernel forms it) to the
+  layer's bf16 bar: mean |delta| <= 2e-3 and relative L2 <= 1e-2 on the differences,
+  max |delta| <= 1.5e-2 on the part of each difference beyond the oracle's allowance.
+  Both sides quantize Q, K and V to the same codes; the FP8 matrix-core products
+  accumulate with less than fp32 precision (measured: up to 2^-11.2 of the largest
+  term), so a P code whose argument lies that close to an E4M3 rounding midpoint may
+  come out one step apart; the allowance is the most such codes can move each output
+  element.
 - Edges: ragged and empty lengths, batches of different lengths, buffer tails of NaN.
 """
 import math
@@ -23,8 +27,8 @@ from long_sequence_attention_h3_amd import binding as B
 from long_sequence_attention_h3_amd import workloads as W
 from oracle import oracle as O
 
-from parity_helpers import (assert_close, assert_tail_zero, gpu_rope, oracle_rope, rows_of,
-                            say, scale_of, to_dev)
+from parity_helpers import (assert_close, assert_close_allow, assert_tail_zero, gpu_rope,
+                            oracle_rope, rows_of, say, scale_of, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,14 +91,19 @@ def gpu_layer_fp8(w, d, **kw):
     return out
 
 
-def oracle_fp8(w, inp, rows, entry, batch=0):
+def oracle_fp8(w, inp, rows, entry, batch=0, skip=0.0, w_head_stride=0, w_q=None, w_k=None):
+    """(output, allowance) of the FP8 oracle on the given rows."""
     q, k, v = (W.bits(inp[x][batch]) for x in ("q", "k", "v"))
     n = inp["n_valid"][batch]
     rows = np.asarray(rows, dtype=np.int64)
     if entry == "varlen":
-        return O.attn_varlen_fp8(q, k, v, n, scale_of(w), rows)
-    return O.attn_layer_fp8(q, k, v, n, W.bits(inp["w_q"]), W.bits(inp["w_k"]), w.eps,
-                            oracle_rope(w), scale_of(w), rows)
+        return O.attn_varlen_fp8(q, k, v, n, scale_of(w), rows, skip_threshold=skip,
+                                 with_allowance=True)
+    wq = W.bits(inp["w_q"] if w_q is None else w_q)
+    wk = W.bits(inp["w_k"] if w_k is None else w_k)
+    return O.attn_layer_fp8(q, k, v, n, wq, wk, w.eps, oracle_rope(w), scale_of(w), rows,
+                            w_head_stride=w_head_stride, skip_threshold=skip,
+                            with_allowance=True)
 
 
 @pytest.mark.parametrize("cfg", [0, 1])
@@ -159,8 +168,8 @@ def test_fp8_matches_oracle(cfg, entry, dev):
     per = ROWS_PER_HEAD[cfg]
     rows = list(range(w.n_valid)) if per is None else W.sample_rows(w, per, 30_000 + cfg)
     say(f"  oracle on {len(rows)} rows x {w.heads} heads")
-    ref = oracle_fp8(w, inp, rows, entry)
-    assert_close(rows_of(out, rows), ref, f"{entry}_fp8 cfg{cfg}")
+    ref, allow = oracle_fp8(w, inp, rows, entry)
+    assert_close_allow(rows_of(out, rows), ref, allow, f"{entry}_fp8 cfg{cfg}")
 
 
 def test_fp8_is_quantized_but_close_to_exact_attention(dev):
@@ -193,8 +202,9 @@ def test_fp8_ragged_lengths_and_batches(n_valid, dev):
                 continue
             rows = list(range(n))
             wb = W.Workload("edge", heads=3, n_valid=n, seq_buf=320, n_1d=None)
-            ref = oracle_fp8(wb, inp, rows, entry, batch=b)
-            assert_close(rows_of(out, rows, batch=b), ref, f"{entry}_fp8 N={n} b={b}")
+            ref, allow = oracle_fp8(wb, inp, rows, entry, batch=b)
+            assert_close_allow(rows_of(out, rows, batch=b), ref, allow,
+                               f"{entry}_fp8 N={n} b={b}")
 
 
 def test_fp8_single_key_returns_dequantized_value(dev):
@@ -280,13 +290,8 @@ def test_fp8_skip_softmax_matches_oracle(alpha, lam, entry, dev):
     say(f"  {entry} lambda={lam}: {skipped} wave tiles skipped ({100 * rate:.1f} %)")
     assert_tail_zero(out, inp["n_valid"], entry)
     rows = np.arange(w.n_valid)
-    q, k, v = (W.bits(inp[x][0]) for x in ("q", "k", "v"))
-    if entry == "varlen":
-        ref = O.attn_varlen_fp8(q, k, v, w.n_valid, scale_of(w), rows, skip_threshold=lam)
-    else:
-        ref = O.attn_layer_fp8(q, k, v, w.n_valid, W.bits(inp["w_q"]), W.bits(inp["w_k"]),
-                               w.eps, oracle_rope(w), scale_of(w), rows, skip_threshold=lam)
-    assert_close(rows_of(out, rows), ref, f"{entry}_fp8 skip {lam}")
+    ref, allow = oracle_fp8(w, inp, rows, entry, skip=lam)
+    assert_close_allow(rows_of(out, rows), ref, allow, f"{entry}_fp8 skip {lam}")
     assert not torch.equal(out.view(torch.int16), dense.view(torch.int16)), "nothing dropped"
     if alpha >= 10.0:
         assert rate > 0.1, rate  # whole wave tiles were skipped
@@ -332,8 +337,54 @@ def test_fp8_skip_full_length_sampled(dev):
     skipped, rate = skip_rate(ws, d["q"], w.n_valid)
     say(f"  layer_fp8 full length, lambda=0.01: {100 * rate:.1f} % of wave tiles skipped")
     rows = W.sample_rows(w, 128, 40_002)
-    q, k, v = (W.bits(inp[x][0]) for x in ("q", "k", "v"))
-    ref = O.attn_layer_fp8(q, k, v, w.n_valid, W.bits(inp["w_q"]), W.bits(inp["w_k"]), w.eps,
-                           oracle_rope(w), scale_of(w), np.asarray(rows), skip_threshold=0.01)
-    assert_close(rows_of(out, rows), ref, "layer_fp8 skip full length")
+    ref, allow = oracle_fp8(w, inp, rows, "layer", skip=0.01)
+    assert_close_allow(rows_of(out, rows), ref, allow, "layer_fp8 skip full length")
     assert rate > 0.1, rate
+
+
+# ---------------------------------------------------------------- layouts and large scores
+def test_fp8_fused_qkv_buffer_row_stride(dev):
+    """Q, K and V as views of one [S, 3, H, D] buffer (row stride 3*H*D): same result as
+    contiguous inputs, bit for bit, and the oracle's."""
+    w = W.Workload("qkv_4h_900of1000", heads=4, n_valid=900, seq_buf=1000, seed=54)
+    inp = W.generate(w, tail="nan")
+    qkv = torch.stack([inp["q"][0], inp["k"][0], inp["v"][0]], dim=1).to(dev)  # [S,3,H,D]
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    assert q.stride(0) == 3 * 4 * 128
+    out = B.attn_layer_fp8(q, k, v, inp["w_q"].to(dev), inp["w_k"].to(dev), 900, w.eps,
+                           gpu_rope(w), scale_of(w))
+    torch.cuda.synchronize()
+    ref = gpu_layer_fp8(w, to_dev(inp, dev))
+    assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16))
+    rows = list(range(900))
+    ref, allow = oracle_fp8(w, inp, rows, "layer")
+    assert_close_allow(rows_of(out.unsqueeze(0), rows), ref, allow, "fused QKV fp8")
+
+
+def test_fp8_per_head_norm_weights(dev):
+    """w_head_stride = D: head h normalises with its own weights (then quantizes)."""
+    w = W.Workload("heads_3h_500of512", heads=3, n_valid=500, seq_buf=512, seed=55)
+    inp = W.generate(w, tail="nan")
+    g = torch.Generator().manual_seed(56)
+    wq = (1 + 0.3 * torch.randn((3, 128), generator=g)).to(torch.bfloat16)
+    wk = (1 + 0.3 * torch.randn((3, 128), generator=g)).to(torch.bfloat16)
+    d = to_dev(inp, dev)
+    out = B.attn_layer_fp8(d["q"], d["k"], d["v"], wq.to(dev), wk.to(dev), 500, w.eps,
+                           gpu_rope(w), scale_of(w))
+    torch.cuda.synchronize()
+    rows = np.arange(500)
+    ref, allow = oracle_fp8(w, inp, rows, "layer", w_head_stride=128, w_q=wq, w_k=wk)
+    assert_close_allow(rows_of(out, rows), ref, allow, "per-head weights fp8")
+
+
+def test_fp8_large_scores_raise_the_running_max_often(dev):
+    """Raw Q scaled by 6 (scores std ~6): each row's running maximum is raised on many
+    tiles, so O and the row sums are carried over repeatedly; tiles are quantized against
+    very different maxima."""
+    w = W.Workload("peaked_2h_2000of2048", heads=2, n_valid=2000, seq_buf=2048, seed=57)
+    inp = W.generate(w, tail="nan")
+    inp["q"] = (inp["q"].float() * 6.0).to(torch.bfloat16)  # the NaN tail stays NaN
+    out = gpu_varlen_fp8(w, to_dev(inp, dev))
+    rows = np.arange(2000)
+    ref, allow = oracle_fp8(w, inp, rows, "varlen")
+    assert_close_allow(rows_of(out, rows), ref, allow, "peaked fp8")
