@@ -7,14 +7,16 @@
 // RMSNorm + RoPE prologue is fused (the Q half here, in registers).
 //
 // Where the time goes (measured on gfx950).  With 32 query rows per wave, every
-// 32x32x16 MFMA consumes one 1 KiB operand read from LDS; at the full MFMA rate a CU
-// would need about as many LDS bytes per cycle as the LDS delivers, and these reads,
-// with the tile copies into LDS, are the main limit.  VALU work of the softmax overlaps
-// the MFMAs only in part (per MFMA, one exp2 costs a few percent of MFMA throughput).
-// Holding 64 rows per wave halves the LDS reads per MFMA but needs one wave per SIMD,
-// which leaves every barrier and memory wait unhidden; it measured slower.  Spreading
-// the softmax work evenly over all 32 MFMA slots of a step, or summing the rows with
-// plain adds instead of v_dot2_f32_bf16, measured no faster either.
+// 32x32x16 MFMA consumes one 1 KiB operand read from LDS.  That is under half of what
+// the LDS delivers (about 190 B per clock per CU with 8 waves), but the reads, the
+// softmax VALU work and the MFMAs compete for issue: MFMA chains with both the reads and
+// this kernel's VALU mix reach about 1,430 TFLOP/s in isolation, and this kernel adds
+// the tile copies into LDS and one barrier per tile on top.  Holding 64 rows per wave
+// halves the LDS reads per MFMA but needs one wave per SIMD, which leaves every barrier
+// and memory wait unhidden; it measured slower.  Spreading the softmax work evenly over
+// all 32 MFMA slots of a step, reading operands further ahead, spreading the tile
+// copies over the step, or summing the rows with plain adds instead of
+// v_dot2_f32_bf16 measured no faster either.
 //
 // The pipeline.  Two waves per SIMD; each wave interleaves the softmax of one 64-key
 // tile with the matrix products of its neighbours.  Per tile j, for its 32 query rows:
