@@ -472,7 +472,9 @@ def main() -> int:
             "kind": "oracle",
             "sample": f"{len(rows)} sampled query rows x {w.heads} heads of {w.name} "
                       f"(all {w.n_valid} keys each), fp64, {t_cpu:.1f} s",
-            "seconds": round(t_cpu, 2), "cpu_model": cpu_model(),
+            "seconds": round(t_cpu, 2),
+            "extrapolated_full_layer_s": round(t_cpu * w.n_valid / len(rows), 1),
+            "cpu_model": cpu_model(),
             "affinity_cpus": len(os.sched_getaffinity(0)),
             "gpu_over_cpu": round(value / (cpu_flops / t_cpu / 1e12), 1),
         }

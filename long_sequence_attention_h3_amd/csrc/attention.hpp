@@ -86,6 +86,15 @@ constexpr int kRows = 32 * kWaves;           // query rows per workgroup
 constexpr int kImageChunks = kTileImageBytes / 1024;  // 1 KiB DMA chunks per tile (35)
 static_assert(kTileImageBytes % 1024 == 0, "tile image must be whole 1 KiB chunks");
 
+// 16 bytes per lane at LDS byte address base + off.  Operand addresses are formed as
+// a scalar slot base plus one per-lane offset, with the constant part `off` folded into
+// the read instruction's offset field.
+__device__ __forceinline__ bf16x8 lds16(uint32_t base, int off) {
+  typedef __attribute__((address_space(3))) const char lds_char;
+  return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
+      (lds_char*)(uintptr_t)base + off);
+}
+
 struct Wave {
   bf16x8 q[8];      // Q^T B operands
   f32x16 o[4];      // O^T accumulators per 32-channel block
@@ -101,12 +110,12 @@ struct Wave {
 // S^T (64 keys x 32 rows, as two 32-key halves).  `kb_base` = this lane's K operand
 // address in the slot: key row l32, channel chunk hl; the (kb, ks) operand sits at
 // + kb*32 rows + ks*32 bytes.
-__device__ __forceinline__ void qk(const Wave& w, f32x16* s, const char* kb_base) {
+__device__ __forceinline__ void qk(const Wave& w, f32x16* s, uint32_t kb_base) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_base + kb * 32 * kKRowPitch + ks * 32);
+      const bf16x8 a = lds16(kb_base, kb * 32 * kKRowPitch + ks * 32);
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.q[ks], ks == 0 ? f32x16{} : s[kb], 0,
                                                       0, 0);
     }
@@ -115,12 +124,12 @@ __device__ __forceinline__ void qk(const Wave& w, f32x16* s, const char* kb_base
 
 // O^T += V^T P^T.  `vb_base` = this lane's V operand address: channel row l32, key chunk hl;
 // the (db, t) operand sits at + db*32 rows + t*32 bytes.
-__device__ __forceinline__ void pv(Wave& w, const char* vb_base) {
+__device__ __forceinline__ void pv(Wave& w, uint32_t vb_base) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb_base + db * 32 * kVRowPitch + t * 32);
+      const bf16x8 a = lds16(vb_base, db * 32 * kVRowPitch + t * 32);
       w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.p[t], w.o[db], 0, 0, 0);
     }
   }
@@ -200,16 +209,14 @@ __device__ __forceinline__ void mx_first(Wave& w, const f32x16* s) {
 // work (which it otherwise does, leaving MFMAs waiting on reads and VALU unhidden).
 template <bool kCheck>
 __device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
-                                            const char* kbase, const char* vbase,
+                                            uint32_t kbase, uint32_t vbase,
                                             float& vmax) {
   bf16x8 kop[16], vop[16];
   auto read_k = [&](int i) {  // operand of QK MFMA i: kb = i & 1, ks = i >> 1
-    kop[i] = *reinterpret_cast<const bf16x8*>(kbase + (i & 1) * 32 * kKRowPitch +
-                                              (i >> 1) * 32);
+    kop[i] = lds16(kbase, (i & 1) * 32 * kKRowPitch + (i >> 1) * 32);
   };
   auto read_v = [&](int i) {  // operand of PV MFMA i: t = i >> 2, db = i & 3
-    vop[i] = *reinterpret_cast<const bf16x8*>(vbase + (i & 3) * 32 * kVRowPitch +
-                                              (i >> 2) * 32);
+    vop[i] = lds16(vbase, (i & 3) * 32 * kVRowPitch + (i >> 2) * 32);
   };
   auto read = [&](int i) {  // operand i of the step's 32 MFMAs
     if (i < 16)
@@ -430,6 +437,12 @@ attn_fwd_kernel(AttnArgs a) {
   // lane i of a wave writes 16 bytes at the wave's LDS base + 16 i).  Wave w copies the
   // 1 KiB chunks w, w + 8, ... of the 35 KiB image.
   auto slot = [&](int t) __attribute__((always_inline)) { return smem + (t % kSlots) * kTileImageBytes; };
+  // LDS byte address of tile t's slot, on the scalar unit
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  auto slot_addr = [&](int t) __attribute__((always_inline)) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(smem_addr + ((unsigned)t % (unsigned)kSlots) * (unsigned)kTileImageBytes));
+  };
   auto load = [&](int t) __attribute__((always_inline)) {
     const char* src = img + (int64_t)t * kTileImageBytes;
     char* dst = slot(t);
@@ -446,8 +459,8 @@ attn_fwd_kernel(AttnArgs a) {
 
 
   // per-lane operand offsets within a slot (see qk / pv)
-  const int k_lane = l32 * kKRowPitch + hl * 16;
-  const int v_lane = kKImageBytes + l32 * kVRowPitch + hl * 16;
+  const uint32_t k_lane = l32 * kKRowPitch + hl * 16;
+  const uint32_t v_lane = kKImageBytes + l32 * kVRowPitch + hl * 16;
 
   // Keys >= tail of the last tile get -inf scores (so p = 0); register 4i+j of half kb
   // holds key kb*32 + 8i + 4hl + j.  Applied after the product, once per workgroup.
@@ -475,7 +488,7 @@ attn_fwd_kernel(AttnArgs a) {
     if (j + kSlots - 1 < nt) load(j + kSlots - 1);  // into the slot tile j-1 left
     if (kNext) {
       float v;
-      steady_step<kChk>(w, cur, nxt, slot(j + 1) + k_lane, slot(j) + v_lane, v);
+      steady_step<kChk>(w, cur, nxt, slot_addr(j + 1) + k_lane, slot_addr(j) + v_lane, v);
       if (kMask) {
         mask_tail(nxt);
         if (kChk) {  // the max taken in the step saw the masked keys: take it again
@@ -490,7 +503,7 @@ attn_fwd_kernel(AttnArgs a) {
     } else {  // last tile: no next scores
       ex(w, cur);
       cv(w, cur);
-      pv(w, slot(j) + v_lane);
+      pv(w, slot_addr(j) + v_lane);
     }
     loads_done();  // tile j+2 in LDS before the next step
     __syncthreads();
@@ -505,7 +518,7 @@ attn_fwd_kernel(AttnArgs a) {
   loads_done();
   __syncthreads();
   f32x16 sa[2], sb[2];
-  qk(w, sa, slot(0) + k_lane);
+  qk(w, sa, slot_addr(0) + k_lane);
   if (nt == 1) mask_tail(sa);
   mx_first(w, sa);  // the running max starts at tile 0's row max
 

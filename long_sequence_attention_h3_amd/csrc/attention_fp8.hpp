@@ -17,7 +17,8 @@
 //      maximum of the scaled scores through tile t (log2 units, c = softmax_scale *
 //      log2(e) * sq * sk), P = E4M3(2^(8 + c s - m_t)) <= 256; O and the row sums are
 //      carried to a new maximum by 2^(m_(t-1) - m_t).  The row sums are the sums of the
-//      quantized P, taken by one extra FP8 product with an all-ones operand.
+//      quantized P, taken by one extra matrix product of P with an all-ones operand
+//      (FP4 E2M1 ones, exact, half the registers of FP8 ones).
 //   O = s_v * (P V) / l, rounded to bf16; rows in [N, S) are zero.
 //   Skip-Softmax (same section: tiles judged unimportant from the QK result skip the
 //      softmax and the P V product; a higher threshold skips more): with threshold
@@ -63,6 +64,22 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t old) {
 __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
   auto q = [&](float x) { return fminf(kMax, fmaxf(-kMax, x * inv)); };
   return cvt2<true>(q(c), q(d), cvt2<false>(q(a), q(b), 0u));
+}
+
+// Column sums of b: FP4 (E2M1) A operand `ones` x E4M3 B, unit scales.
+__device__ __forceinline__ f32x16 mfma_ones(i32x8 ones, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, b, c, 4, 0, 0, 127, 0, 127);
+}
+
+// max(a, b) for scores that are finite or -inf: the NaN-propagating maximum
+// (v_maximum3_f32) then equals fmaxf, and unlike fmaxf needs no input canonicalization.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// vmax over the lane pair (l, l ^ 32); identical bits in both lanes.
+__device__ __forceinline__ float pair_vmax(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                            false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
@@ -368,9 +385,9 @@ attn_fp8_kernel(Fp8AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
   w.l = f32x16{};
-  i32x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;  // E4M3 1.0 in every byte
+  // the row-sum product's A operand: 1.0 in FP4 E2M1 (code 0x2) in every nibble; an FP4
+  // operand occupies the first 4 dwords
+  const i32x8 ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
 
   const int nt = (int)((a.n_valid + kTileKeys - 1) / kTileKeys);
   const char* img = a.img + (int64_t)head * a.tiles_per_head * kTileBytes;
@@ -446,11 +463,11 @@ attn_fp8_kernel(Fp8AttnArgs a) {
         } else {
           float gm = s[kb][8 * g];
 #pragma unroll
-          for (int r = 8 * g + 1; r < 8 * g + 8; ++r) gm = fmaxf(gm, s[kb][r]);
-          v = fmaxf(v, gm * cb[2 * kb + g]);
+          for (int r = 8 * g + 1; r < 8 * g + 8; ++r) gm = fp8::vmax(gm, s[kb][r]);
+          v = fp8::vmax(v, gm * cb[2 * kb + g]);
         }
       }
-    v = pair_max(v);
+    v = fp8::pair_vmax(v);
     if (kSkip) {  // decided against the maximum before this tile; rows >= N never block
       w.skip = !row_valid || v < w.m + a.skip_log2;
       w.skip_all = __builtin_amdgcn_ballot_w64(!w.skip) == 0;
@@ -484,7 +501,10 @@ attn_fp8_kernel(Fp8AttnArgs a) {
         const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], cb[2 * kb + (r >> 3)], off));
         p[jj] = (kMask && key_of(kb, r) >= tail) ? 0.0f : x;
       }
-      w.p[4 * kb + i] = (int)fp8::cvt2<true>(p[2], p[3], fp8::cvt2<false>(p[0], p[1], 0u));
+      // both halves of the word are written: the previous codes serve as the untouched
+      // half of the first conversion, which saves clearing a register
+      w.p[4 * kb + i] = (int)fp8::cvt2<true>(
+          p[2], p[3], fp8::cvt2<false>(p[0], p[1], (uint32_t)w.p[4 * kb + i]));
     }
   };
 
@@ -493,7 +513,7 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     const uint32_t vb = slot_addr(t) + v_lane;
 #pragma unroll
     for (int db = 0; db < 4; ++db) w.o[db] = fp8::mfma8(read32(vb, db * 32 * kVPitch), w.p, w.o[db]);
-    w.l = fp8::mfma8(ones, w.p, w.l);
+    w.l = fp8::mfma_ones(ones, w.p, w.l);
   };
 
   // One step for tile j: `cur` holds tile j's scores (its max already applied), `nxt`
