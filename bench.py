@@ -199,7 +199,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the layer is "
-              "measured on one GPU's share; multi-GPU sharding is not part of this build.",
+              "measured on one GPU's share (a head-sharded multi-GPU layer is not implemented).",
               file=sys.stderr)
         return 2
 
