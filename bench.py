@@ -311,6 +311,22 @@ def main() -> int:
     log(f"[bench] kv_pack {ms_pack:.3f} ms ({pack_bytes / ms_pack / 1e6:.0f} GB/s), "
         f"qk_rmsnorm_rope {ms_prol:.3f} ms ({prol_bytes / ms_prol / 1e6:.0f} GB/s)")
 
+    # ---- large scores: Q/K weights x6 put every workgroup outside the fast pass's score
+    # bound, so the checked pass (per-tile running max) does all the work
+    w_q6 = (d["w_q"].float() * 6.0).to(torch.bfloat16)
+    w_k6 = (d["w_k"].float() * 6.0).to(torch.bfloat16)
+    ms_big = timed(lambda: B.attn_layer(d["q"], d["k"], d["v"], w_q6, w_k6, n, w.eps, rope,
+                                        scale, out=out, workspace=ws), args.steps)
+    valid_blocks = (w.n_valid + 255) // 256
+    big_checked = float(B.pass_flags(ws, d["q"])[:, :, :valid_blocks].float().mean())
+    large_scores = {"weights": "w_q, w_k x 6", "ms_per_step": round(ms_big, 4),
+                    "tflops": round(flops / ms_big / 1e9, 2),
+                    "workgroups_in_checked_pass": round(big_checked, 4)}
+    del w_q6, w_k6
+    log(f"[bench] large scores (w x 6): h3_attn_layer {ms_big:.3f} ms "
+        f"({flops / ms_big / 1e9:.1f} TFLOP/s), {100 * big_checked:.1f} % of workgroups "
+        f"in the checked pass")
+
     # ---- the FP8 (SAGE) variant on the same workload
     ws8 = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
     out8 = torch.empty_like(d["q"])
@@ -424,6 +440,7 @@ def main() -> int:
                      "kernel_ms": round(ms_attn, 4),
                      "timed": "h3_attn_packed: fast pass + checked pass, HIP events on "
                               "the launch stream"},
+        "large_scores_checked_pass": large_scores,
         "kernels": {
             "kv_pack_kernel": {"ms": round(ms_pack, 4), "bytes": pack_bytes,
                                "GB/s": round(pack_bytes / ms_pack / 1e6, 1),

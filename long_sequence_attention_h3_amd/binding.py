@@ -353,6 +353,18 @@ def attn_packed_fp8(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: 
     return out
 
 
+def pass_flags(workspace, x: torch.Tensor) -> torch.Tensor:
+    """Which pass handled each 256-row workgroup in the last bf16 attention call with
+    ``workspace`` for a tensor shaped like ``x``: [B, H, ceil(S / 256)] int32, 0 = the
+    fast pass (scores provably bounded), 1 = the checked pass (layout documented with
+    h3_attn_workspace_size)."""
+    B, S, H, D = _dims(x)
+    img = B * H * ((S + 63) // 64) * 35840
+    blocks = (S + 255) // 256
+    n = B * H * blocks
+    return workspace[img: img + 4 * n].view(torch.int32).view(B, H, blocks)
+
+
 def fp8_skip_counts(workspace, x: torch.Tensor) -> torch.Tensor:
     """Skip counts the last FP8 attention call left in ``workspace`` for a tensor shaped
     like ``x``: [B, H, ceil(S / 256)] int32, wave tiles (32 rows x 64 keys) skipped per

@@ -126,7 +126,14 @@ def test_large_scores_mix_both_passes(dev):
     inp["k"][0, 1400] = (inp["k"][0, 1400].float() * 3).to(torch.bfloat16)
     d = to_dev(inp, dev)
     say("[edge] large scores, varlen")
-    out = gpu_varlen(w, d)
+    ws = torch.empty(B.workspace_size(d["q"]), dtype=torch.uint8, device=dev)
+    out = gpu_varlen(w, d, workspace=ws)
+    # rows [256, 512) of both heads were left to the checked pass, every other workgroup
+    # was finished by the fast pass
+    flags = B.pass_flags(ws, d["q"]).cpu()
+    want = torch.zeros_like(flags)
+    want[:, :, 1] = 1
+    assert torch.equal(flags, want), flags
     assert_tail_zero(out, [n], "large scores varlen")
     rows = list(range(n))
     assert_close(rows_of(out, rows), oracle_varlen(w, inp, rows), "large scores varlen")
