@@ -366,3 +366,62 @@ def test_allowance_zero_without_near_midpoint_weights_and_bounded_otherwise():
                                    with_allowance=True)
     assert np.all(np.isfinite(allow)) and np.all(allow >= 0.0)
     assert allow.mean() < 0.05 * np.abs(out).mean() + 1e-3
+
+
+def _two_key_case(alpha, **kw):
+    """Query alpha * e_0 against keys e_0 and 0 (one 16-key block, amax 1), V rows 0 and
+    e_5.  In log2 units the key-0 score exceeds the key-1 score (0) by
+    alpha * fl(scale * log2 e), exactly as the codes are 448 and 0."""
+    D = 128
+    q = np.zeros((2, 1, D))
+    q[:, 0, 0] = alpha
+    k = np.zeros((2, 1, D))
+    k[0, 0, 0] = 1.0
+    v = np.zeros((2, 1, D))
+    v[1, 0, 5] = 1.0
+    return O.attn_varlen_fp8(bf16(q), bf16(k), bf16(v), 2, 1 / math.sqrt(D), np.array([0]),
+                             with_allowance=True, **kw)
+
+
+def test_p_is_256_times_the_weight_down_to_the_smallest_subnormal():
+    """P = E4M3(256 * 2^(x - m)): a key 17.47 log2 units below the maximum gets
+    2^(8 - 17.47), 0.72 of the smallest E4M3 subnormal 2^-9, which rounds up to 2^-9, so
+    o_5 = 2^-9 / (256 + 2^-9).  Any other power-of-two factor in
+    front of the weights moves this key across the subnormal rounding point (at 128 it
+    rounds to 0), so only the factor 256 gives this output."""
+    out, _ = _two_key_case(137.0)
+    want = np.zeros(128)
+    want[5] = 2.0 ** -9 / (256 + 2.0 ** -9)
+    assert np.allclose(out[0, 0], want, rtol=1e-12, atol=0)
+
+
+def test_allowance_of_a_code_at_an_e4m3_midpoint():
+    """Key 1's weight 2^(8 - 1.4744) = 92.13 lies 0.14 % above the 88/96 midpoint 92, inside
+    the score-error window of the maximum (2^-9 of its 1.47 log2 units): the code is 96
+    (o_5 = 96 / 352), and the allowance is one step of 8 carried to the output,
+    8 * |v_1 - o| / (256 + 88) with the smaller of the two normalisers."""
+    out, allow = _two_key_case(11.5625)
+    o5 = 96.0 / (256 + 96)
+    assert abs(out[0, 0, 5] - o5) <= 1e-15
+    assert abs(allow[0, 0, 5] - 8 * (1 - o5) / (256 + 88)) <= 1e-12
+    assert np.all(allow[0, 0, np.arange(128) != 5] == 0.0)  # V is 0 there, as is o
+
+
+def test_allowance_of_a_skip_decision_at_its_threshold():
+    """One key per tile; key 1 sits g = 1.4744 log2 units below the maximum, its code 96.
+    A threshold 2^(-g + 0.001) lies inside the window (2^-9 of the maximum's 1.47 units)
+    and drops the tile: o_5 = 0, and the allowance is the tile's 96 against the smallest
+    normaliser the flip could leave, 96 / (256 - 96).  At 2^(-g - 0.001) the tile is kept
+    (o_5 = 96/352) with allowance 96 * (1 - 96/352) / 256; at 2^(-g + 0.01), outside the
+    window, the drop is certain and the allowance 0."""
+    g = float(np.float32(11.5625) * np.float32(np.float32(1 / math.sqrt(128)) *
+                                              np.float32(1.4426950408889634)))
+    out, allow = _two_key_case(11.5625, p_tile=1, skip_threshold=2.0 ** (-g + 0.001))
+    assert out[0, 0, 5] == 0.0
+    assert abs(allow[0, 0, 5] - 96.0 / (256 - 96)) <= 1e-12
+    out, allow = _two_key_case(11.5625, p_tile=1, skip_threshold=2.0 ** (-g - 0.001))
+    o5 = 96.0 / 352
+    assert abs(out[0, 0, 5] - o5) <= 1e-15
+    assert abs(allow[0, 0, 5] - 96 * (1 - o5) / 256) <= 1e-12
+    out, allow = _two_key_case(11.5625, p_tile=1, skip_threshold=2.0 ** (-g + 0.01))
+    assert out[0, 0, 5] == 0.0 and np.all(allow == 0.0)
