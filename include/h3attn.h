@@ -109,9 +109,10 @@ h3_status h3_qk_rmsnorm_rope(const void* q_in, const void* k_in, void* q_out, vo
  * is invalid).  The workspace holds the key and value operands of every batch repacked
  * for the attention kernel as 64-key tiles of 35,840 bytes each,
  * B * H * ceil(S / 64) * 35840 bytes (about 1.09x the bf16 size of K plus V), followed
- * by one 4-byte word per 256 query rows of every head and batch (which of the two
- * attention passes handles those rows), rounded up to 256 bytes:
- * round_up(B * H * ceil(S / 256) * 4, 256) bytes. */
+ * by one 4-byte word per 256 query rows of every head and batch, rounded up to 256
+ * bytes: round_up(B * H * ceil(S / 256) * 4, 256) bytes.  After an attention call,
+ * word (b * H + h) * ceil(S / 256) + i tells which pass handled rows [256 i, 256 i + 256)
+ * of head h, batch b: 0 the fast pass (scores provably bounded), 1 the checked pass. */
 size_t h3_attn_workspace_size(const h3_shape* shape);
 
 /* Stage 1 of attention: repack K and V of every batch into `workspace` (keys of 64-key
@@ -173,7 +174,9 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
  * are those of a streaming softmax over 64-key tiles: P = E4M3(256 exp(s - m_t)) with
  * m_t the running row maximum through the key's tile, earlier sums carried over by
  * exp(m_(t-1) - m_t); each row is normalised by the sum of its quantized weights.
- * Products accumulate in fp32; output rounded to bf16.  Deterministic run to run.
+ * Products accumulate into fp32 (the FP8 matrix cores sum each 64-term product with
+ * an error of up to about 2^-11 of its largest term); output rounded to bf16.
+ * Deterministic run to run.
  * Accuracy: a few percent relative to exact attention (FP8 keeps 4 significant bits).
  *
  * Skip-Softmax ([Blog §4.3], figure 6: a tile-level decision from the QK result skips
