@@ -9,10 +9,14 @@
 //   y  = (x - mean) / sqrt(var + eps) * (1 + scale) + shift      (bf16 out)
 // over the `hidden` channels of each valid token, with the population variance.
 //
-// One workgroup of 256 threads per token; each thread holds up to kMaxChunks chunks of
-// 8 channels in registers, so the row is read from HBM once and the variance is taken
-// in a second pass over registers (no cancellation).  HBM-bound: per token it reads
-// 4C bytes of x (+ 2C of a) and writes 2C of y (+ 4C of x).
+// One workgroup of 256 threads per group of consecutive tokens, taken one after the
+// other: 4 with the residual update, whose threads then keep their channels' gate,
+// shift and scale in registers for the whole group (read once per group, not per
+// token), 1 without it (measured: holding them costs the lighter variant more in
+// occupancy than it saves).  Each thread holds up to kMaxChunks chunks of 8 channels of
+// the current row, so the row is read from HBM once and the variance is taken in a
+// second pass over registers (no cancellation).
+// HBM-bound: per token it reads 4C bytes of x (+ 2C of a) and writes 2C of y (+ 4C of x).
 #pragma once
 
 #include "common.hpp"
@@ -28,12 +32,15 @@ struct BlockArgs {
   __bf16* y;             // [S, C]
   int64_t hidden;        // C, a multiple of 8, at most 8 * 256 * kMaxChunks
   int64_t n_valid;
+  int64_t seq_buf;       // S
   float eps;
 };
 
 namespace blk {
 constexpr int kThreads = 256;
 constexpr int kMaxChunks = 4;  // 8-channel chunks per thread: C <= 8,192
+constexpr int kRowsResidual = 4;  // rows per workgroup with the residual update
+constexpr int kRowsPlain = 1;     // rows per workgroup without it
 }  // namespace blk
 
 // Sum over the workgroup (256 threads = 4 waves), identical in every thread.
@@ -47,88 +54,104 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-template <bool kResidual, bool kGate>
+// kRows consecutive rows per workgroup.  With kRows > 1 each thread loads its slices of
+// gate, shift and scale once and keeps them in registers for all the rows; with
+// kRows = 1 it loads them where they are used (fewer live registers, more waves).
+template <bool kResidual, bool kGate, int kRows>
 __global__ __launch_bounds__(blk::kThreads) void residual_norm_modulate_kernel(BlockArgs a) {
   using namespace blk;
-  const int64_t row = blockIdx.x;
+  constexpr bool kHold = kRows > 1;
   const int tid = threadIdx.x;
   const int nchunk = (int)(a.hidden / 8);
-  __bf16* yrow = a.y + row * a.hidden;
-  if (row >= a.n_valid) {  // rows past the valid length: y = 0, x untouched
-    for (int c = tid; c < nchunk; c += kThreads)
-      *reinterpret_cast<u32x4*>(yrow + c * 8) = u32x4{0u, 0u, 0u, 0u};
-    return;
-  }
-  float* xrow = a.x + row * a.hidden;
   __shared__ float red[4];
 
-  float v[kMaxChunks][8];
-  float sum = 0.0f;
+  // 8 consecutive fp32 values of a modulation vector
+  auto load8 = [&](const float* p, int c, float* out) __attribute__((always_inline)) {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p + c * 8);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + c * 8 + 4);
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = tid + i * kThreads;
-    if (c < nchunk) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(xrow + c * 8);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(xrow + c * 8 + 4);
+    for (int e = 0; e < 4; ++e) {
+      out[e] = lo[e];
+      out[4 + e] = hi[e];
+    }
+  };
+  float g[kMaxChunks][8], sh[kMaxChunks][8], sc[kMaxChunks][8];
+  if (kHold) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[i][e] = x0[e];
-        v[i][4 + e] = x1[e];
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < nchunk) {
+        if (kGate) load8(a.gate, c, g[i]);
+        load8(a.shift, c, sh[i]);
+        load8(a.scale, c, sc[i]);
       }
-      if (kResidual) {
-        float br[8];
-        unpack8(*reinterpret_cast<const u32x4*>(a.a + row * a.hidden + c * 8), br);
-        float g[8];
-        if (kGate) {
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gate + c * 8);
-          const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gate + c * 8 + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            g[e] = g0[e];
-            g[4 + e] = g1[e];
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[i][e] = kGate ? __builtin_fmaf(g[e], br[e], v[i][e]) : v[i][e] + br[e];
-        *reinterpret_cast<f32x4*>(xrow + c * 8) = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
-        *reinterpret_cast<f32x4*>(xrow + c * 8 + 4) = f32x4{v[i][4], v[i][5], v[i][6], v[i][7]};
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sum += v[i][e];
     }
   }
+
   const float inv_c = 1.0f / (float)a.hidden;
-  const float mean = block_sum(sum, red) * inv_c;
-  float ss = 0.0f;
+  for (int k = 0; k < kRows; ++k) {
+    const int64_t row = (int64_t)blockIdx.x * kRows + k;  // uniform
+    if (row >= a.seq_buf) break;
+    __bf16* yrow = a.y + row * a.hidden;
+    if (row >= a.n_valid) {  // rows past the valid length: y = 0, x untouched
+      for (int c = tid; c < nchunk; c += kThreads)
+        *reinterpret_cast<u32x4*>(yrow + c * 8) = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
+    float* xrow = a.x + row * a.hidden;
+    float v[kMaxChunks][8];
+    float sum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = tid + i * kThreads;
-    if (c < nchunk)
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < nchunk) {
+        load8(xrow, c, v[i]);
+        if (kResidual) {
+          float br[8];
+          unpack8(*reinterpret_cast<const u32x4*>(a.a + row * a.hidden + c * 8), br);
+          float gi[8];
+          if (kGate && !kHold) load8(a.gate, c, gi);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = v[i][e] - mean;
-        ss = __builtin_fmaf(d, d, ss);
+          for (int e = 0; e < 8; ++e)
+            v[i][e] = kGate ? __builtin_fmaf(kHold ? g[i][e] : gi[e], br[e], v[i][e])
+                            : v[i][e] + br[e];
+          *reinterpret_cast<f32x4*>(xrow + c * 8) = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
+          *reinterpret_cast<f32x4*>(xrow + c * 8 + 4) = f32x4{v[i][4], v[i][5], v[i][6], v[i][7]};
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += v[i][e];
       }
-  }
-  const float var = block_sum(ss, red) * inv_c;
-  const float inv = 1.0f / sqrtf(var + a.eps);
+    }
+    const float mean = block_sum(sum, red) * inv_c;
+    float ss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = tid + i * kThreads;
-    if (c < nchunk) {
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(a.scale + c * 8);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(a.scale + c * 8 + 4);
-      const f32x4 h0 = *reinterpret_cast<const f32x4*>(a.shift + c * 8);
-      const f32x4 h1 = *reinterpret_cast<const f32x4*>(a.shift + c * 8 + 4);
-      float out[8];
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < nchunk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float sc = e < 4 ? s0[e] : s1[e - 4];
-        const float sh = e < 4 ? h0[e] : h1[e - 4];
-        out[e] = __builtin_fmaf((v[i][e] - mean) * inv, 1.0f + sc, sh);
+        for (int e = 0; e < 8; ++e) {
+          const float d = v[i][e] - mean;
+          ss = __builtin_fmaf(d, d, ss);
+        }
+    }
+    const float var = block_sum(ss, red) * inv_c;
+    const float inv = 1.0f / sqrtf(var + a.eps);
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = tid + i * kThreads;
+      if (c < nchunk) {
+        float sci[8], shi[8];
+        if (!kHold) {
+          load8(a.scale, c, sci);
+          load8(a.shift, c, shi);
+        }
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          out[e] = __builtin_fmaf((v[i][e] - mean) * inv, 1.0f + (kHold ? sc[i][e] : sci[e]),
+                                  kHold ? sh[i][e] : shi[e]);
+        *reinterpret_cast<u32x4*>(yrow + c * 8) = pack8(out);
       }
-      *reinterpret_cast<u32x4*>(yrow + c * 8) = pack8(out);
     }
   }
 }

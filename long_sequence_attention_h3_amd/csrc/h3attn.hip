@@ -558,14 +558,17 @@ h3_status h3_residual_norm_modulate(void* x, const void* a, const float* gate,
     ba.y = static_cast<__bf16*>(y) + b * S * C;
     ba.hidden = C;
     ba.n_valid = rows->seq_valid[b];
+    ba.seq_buf = S;
     ba.eps = eps;
-    const unsigned grid = (unsigned)S;
+    constexpr int RR = blk::kRowsResidual, RP = blk::kRowsPlain;
+    const unsigned grid_r = (unsigned)((S + RR - 1) / RR);
+    const unsigned grid_p = (unsigned)((S + RP - 1) / RP);
     if (a && gate)
-      residual_norm_modulate_kernel<true, true><<<grid, blk::kThreads, 0, stream>>>(ba);
+      residual_norm_modulate_kernel<true, true, RR><<<grid_r, blk::kThreads, 0, stream>>>(ba);
     else if (a)
-      residual_norm_modulate_kernel<true, false><<<grid, blk::kThreads, 0, stream>>>(ba);
+      residual_norm_modulate_kernel<true, false, RR><<<grid_r, blk::kThreads, 0, stream>>>(ba);
     else
-      residual_norm_modulate_kernel<false, false><<<grid, blk::kThreads, 0, stream>>>(ba);
+      residual_norm_modulate_kernel<false, false, RP><<<grid_p, blk::kThreads, 0, stream>>>(ba);
     H3_TRY(launched());
   }
   return H3_OK;
