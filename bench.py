@@ -236,7 +236,8 @@ def main() -> int:
                      out=out, workspace=ws)
 
     if args.only == "attn":
-        B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps, rope=rope)
+        B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps, rope=rope,
+                  softmax_scale=scale)
         for i in range(args.steps):
             B.attn_packed(d["q"], ws, n, scale, w_q=d["w_q"], eps=w.eps, rope=rope, out=out)
             torch.cuda.synchronize()
@@ -276,7 +277,8 @@ def main() -> int:
     # ---- dominant kernel alone: attention from packed K/V (fused Q prologue).  One call
     # is the fast pass plus the checked pass, which returns at once for workgroups the
     # fast pass finished (all of them on this workload); the events bracket both.
-    B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps, rope=rope)
+    B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps, rope=rope,
+              softmax_scale=scale)
     for _ in range(2):
         B.attn_packed(d["q"], ws, n, scale, w_q=d["w_q"], eps=w.eps, rope=rope, out=out)
     torch.cuda.synchronize()
@@ -306,7 +308,7 @@ def main() -> int:
     tiles = (w.n_valid + 63) // 64
     pack_bytes = 2 * w.n_valid * row_bytes + w.heads * tiles * 35840
     ms_pack = timed(lambda: B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps,
-                                      rope=rope), args.steps)
+                                      rope=rope, softmax_scale=scale), args.steps)
     q2, k2 = torch.empty_like(d["q"]), torch.empty_like(d["k"])
     prol_bytes = 2 * 2 * w.n_valid * row_bytes
     ms_prol = timed(lambda: B.qk_rmsnorm_rope(d["q"], d["k"], d["w_q"], d["w_k"], n, w.eps,

@@ -118,14 +118,22 @@ size_t h3_attn_workspace_size(const h3_shape* shape);
 /* Stage 1 of attention: repack K and V of every batch into `workspace` (keys of 64-key
  * tiles as the attention kernel reads them; keys >= N_b stored as zeros).  With w_k
  * non-NULL each K row is first RMS-normalised (weights w_k, w_head_stride, eps) and
- * rotated (rope), exactly as h3_qk_rmsnorm_rope does; with w_k NULL, K is used as is
- * and rope/eps are ignored.  Reads K and V with in_row_stride.  The packed workspace
- * stays valid for any number of h3_attn_packed calls with the same shape.
- * Errors: H3_ERR_NULL, H3_ERR_SHAPE, H3_ERR_ALIGN, H3_ERR_UNSUPPORTED, H3_ERR_DEVICE,
- * H3_ERR_LAUNCH, H3_ERR_WORKSPACE. */
+ * rotated (rope) with the arithmetic of h3_qk_rmsnorm_rope, then multiplied in fp32 by
+ * softmax_scale * log2(e) and rounded once to bf16, so that the attention kernel's
+ * scores come out of the matrix cores in exp2 units (the layer's K operand is thus
+ * bf16(k * softmax_scale * log2 e) rather than bf16(k): the same relative rounding,
+ * of a different value).  With w_k NULL, K is stored as given and rope, eps and
+ * softmax_scale are ignored.  The tiles record the factor used, and h3_attn_packed
+ * accepts either kind with any softmax_scale.  Reads K and V with in_row_stride.  The
+ * packed workspace stays valid for any number of h3_attn_packed calls with the same
+ * shape.
+ * Errors: H3_ERR_NULL, H3_ERR_SHAPE (also softmax_scale not positive and finite when w_k
+ * is non-NULL), H3_ERR_ALIGN, H3_ERR_UNSUPPORTED, H3_ERR_DEVICE, H3_ERR_LAUNCH,
+ * H3_ERR_WORKSPACE. */
 h3_status h3_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
-                     float eps, const h3_rope* rope, const h3_shape* shape, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream);
+                     float eps, const h3_rope* rope, float softmax_scale,
+                     const h3_shape* shape, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 /* Stage 2 of attention: O = softmax(scale * Q K^T) V over the valid keys, with K and V
  * taken from a workspace filled by h3_kv_pack for the same shape.  With w_q non-NULL
@@ -154,10 +162,13 @@ h3_status h3_attn_varlen(const void* q, const void* k, const void* v, void* o,
                          size_t workspace_bytes, hipStream_t stream);
 
 /* The whole layer: per-head Q/K RMSNorm + RoPE fused into the attention prologue,
- * then attention as in h3_attn_varlen.  Bit-identical to h3_qk_rmsnorm_rope followed
- * by h3_attn_varlen, but normalised Q and K never round-trip through a bf16 [S, H, D]
- * buffer: K is prepared once into the workspace (h3_kv_pack with w_k), Q in registers
- * (h3_attn_packed with w_q).  Inputs are not modified.
+ * then attention as in h3_attn_varlen, with normalised Q and K never round-tripping
+ * through a bf16 [S, H, D] buffer: K is prepared once into the workspace (h3_kv_pack
+ * with w_k, which stores it times softmax_scale * log2(e), rounded once), Q in registers
+ * (h3_attn_packed with w_q).  The Q operands are bit-identical to what
+ * h3_qk_rmsnorm_rope writes; the K operands are bf16(k * softmax_scale * log2 e) instead
+ * of bf16(k), so the result agrees with h3_qk_rmsnorm_rope + h3_attn_varlen to within
+ * bf16 rounding, not bit for bit.  Inputs are not modified.
  * Errors: as h3_attn_varlen. */
 h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
                         const void* w_q, const void* w_k, int64_t w_head_stride, float eps,

@@ -85,7 +85,7 @@ def lib():
         L.h3_qk_rmsnorm_rope.restype = ctypes.c_int
         L.h3_attn_workspace_size.argtypes = [SH]
         L.h3_attn_workspace_size.restype = SZ
-        L.h3_kv_pack.argtypes = [P, P, P, I64, F, RP, SH, P, SZ, P]
+        L.h3_kv_pack.argtypes = [P, P, P, I64, F, RP, F, SH, P, SZ, P]
         L.h3_kv_pack.restype = ctypes.c_int
         L.h3_attn_packed.argtypes = [P, P, P, I64, F, RP, F, SH, P, SZ, P]
         L.h3_attn_packed.restype = ctypes.c_int
@@ -242,9 +242,10 @@ def attn_layer(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_scale
 
 
 def kv_pack(k, v, n_valid, workspace=None, w_k=None, eps: float = 0.0, rope: Rope | None = None,
-            stream=None):
-    """Stage 1 (h3_kv_pack): repack K (normalised + rotated when ``w_k`` is given) and V
-    into a workspace for h3_attn_packed.  Returns the workspace."""
+            softmax_scale: float = 0.0, stream=None):
+    """Stage 1 (h3_kv_pack): repack K (normalised + rotated, then multiplied by
+    ``softmax_scale * log2(e)`` before rounding, when ``w_k`` is given) and V into a
+    workspace for h3_attn_packed.  Returns the workspace."""
     s_in = _row_stride(k, "k")
     if _row_stride(v, "v") != s_in:
         raise ValueError("k and v must share a row stride")
@@ -254,7 +255,8 @@ def kv_pack(k, v, n_valid, workspace=None, w_k=None, eps: float = 0.0, rope: Rop
     st = _stream(k.device) if stream is None else stream
     _check(lib().h3_kv_pack(_p(k), _p(v), _p(w_k), w_head_stride, float(eps),
                             ctypes.byref(rope) if rope is not None else None,
-                            ctypes.byref(call.shape), _p(ws), ws.numel(), ctypes.c_void_p(st)),
+                            float(softmax_scale), ctypes.byref(call.shape), _p(ws), ws.numel(),
+                            ctypes.c_void_p(st)),
            "h3_kv_pack")
     return ws
 

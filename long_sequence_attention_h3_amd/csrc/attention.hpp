@@ -30,13 +30,16 @@
 // and row sums; PV: O^T += V^T P^T.  The scores of tiles j and j+1 live in two register
 // sets used alternately (loop unrolled by two).
 //
-// Arithmetic.  Scores s = q.k are exact bf16 products summed in fp32 (the QK
-// accumulation starts from the inline constant 0), and p = exp2(fma(s, c, -m c)) with
-// c = softmax_scale * log2(e) applied in fp32: one FMA and one exp2 per score.
-// (Pre-scaling Q by c in bf16 would save the FMA but add a score error growing with
-// the logits.)  The running max m is raised only when a score exceeds it by more than
-// kTauP / c, so p <= 2^8 and the O rescale is rare.  Keys >= N of the last tile get
-// -inf scores.  P is rounded to bf16 for the PV product, and the row sums add exactly
+// Arithmetic.  Scores are exact bf16 products summed in fp32.  Two forms, chosen per
+// launch from the factor the K tiles were stored with:
+//  - prescaled K (the layer path: the pre-pass multiplies the normalised fp32 K rows by
+//    c = softmax_scale * log2(e) before their one rounding to bf16): the QK
+//    accumulation of a tile starts at -m, so the matrix cores return c s - m and
+//    p = exp2 of it, with no per-score VALU work besides the exp2 (the fast pass);
+//  - K as given (bf16 input, where scaling would round it a second time): the
+//    accumulation starts at 0 and p = exp2(fma(s, c, -m c)), c applied in fp32.
+// The running max m is raised only when a score exceeds it by more than kTauP / c, so
+// p <= 2^8 and the O rescale is rare.  Keys >= N of the last tile get -inf scores.  P is rounded to bf16 for the PV product, and the row sums add exactly
 // those rounded values (v_dot2_f32_bf16 with (1, 1)), so every output row is a true
 // weighted average of V rows; summing the unrounded fp32 p instead costs up to 2^-9
 // relative error on strongly peaked rows.
@@ -99,11 +102,12 @@ struct Wave {
   bf16x8 q[8];      // Q^T B operands
   f32x16 o[4];      // O^T accumulators per 32-channel block
   bf16x8 p[4];      // P^T B operands per 16-key step
+  f32x16 nm;        // prescaled K: -m in every register, the QK accumulation's start
   float m;          // running max (raw score units)
   float nmc;        // -m * c, the exp2 offset
   float mt;         // m + kTauP / c: scores above it raise the running max
   float l;          // row-sum partial over this lane's keys
-  float c;          // softmax_scale * log2(e)
+  float c;          // raw score units -> exp2 units (1 for prescaled K)
   float tau;        // kTauP / c: the running-max slack in raw units
 };
 
@@ -135,15 +139,18 @@ __device__ __forceinline__ void pv(Wave& w, uint32_t vb_base) {
   }
 }
 
-// E: p = exp2(c (s - m)), in place.
+// E: p = exp2(c (s - m)), in place.  kPre (K prescaled by c): the scores already are
+// c s - m, and p = exp2(s).
+template <bool kPre>
 __device__ __forceinline__ float ex1(const Wave& w, float s) {
-  return __builtin_amdgcn_exp2f(__builtin_fmaf(s, w.c, w.nmc));
+  return kPre ? __builtin_amdgcn_exp2f(s) : __builtin_amdgcn_exp2f(__builtin_fmaf(s, w.c, w.nmc));
 }
+template <bool kPre>
 __device__ __forceinline__ void ex(const Wave& w, f32x16* s) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[kb][e] = ex1(w, s[kb][e]);
+    for (int e = 0; e < 16; ++e) s[kb][e] = ex1<kPre>(w, s[kb][e]);
 }
 
 // Set the running max to v where `need` (wave-uniform call); with kRescale, scale O and
@@ -187,6 +194,17 @@ __device__ __forceinline__ void cv(Wave& w, const f32x16* s) {
   w.l = acc0 + acc1;
 }
 
+// Prescaled K (fast pass only): the scores of the first tile are made relative to the
+// running max (shifted by -d = -m), and the QK accumulation of later tiles starts at -m.
+__device__ __forceinline__ void shift_scores(Wave& w, f32x16* s, float d) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[kb][e] -= d;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) w.nm[e] = -w.m;
+}
+
 // M on the first tile: the running max starts at the tile's row max.
 __device__ __forceinline__ void mx_first(Wave& w, const f32x16* s) {
   float v = s[0][0];
@@ -207,7 +225,7 @@ __device__ __forceinline__ void mx_first(Wave& w, const f32x16* s) {
 //   PV MFMA i:  the last group's convert/sum ops (i < 4), one max3 of tile j+1's scores.
 // A scheduling barrier after each group keeps the compiler from clustering the VALU
 // work (which it otherwise does, leaving MFMAs waiting on reads and VALU unhidden).
-template <bool kCheck>
+template <bool kCheck, bool kPre>
 __device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
                                             uint32_t kbase, uint32_t vbase,
                                             float& vmax) {
@@ -257,11 +275,11 @@ __device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
 #pragma unroll
   for (int i = 0; i < 16; ++i) {  // QK(j+1) || exp(j), convert/sum(j)
     const int kb = i & 1, ks = i >> 1;
-    nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], w.q[ks], ks == 0 ? f32x16{} : nxt[kb],
-                                                      0, 0, 0);
+    nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        kop[i], w.q[ks], ks == 0 ? (kPre ? w.nm : f32x16{}) : nxt[kb], 0, 0, 0);
     read(i + 3);
-    cur[(2 * i) >> 4][(2 * i) & 15] = ex1(w, cur[(2 * i) >> 4][(2 * i) & 15]);
-    cur[(2 * i + 1) >> 4][(2 * i + 1) & 15] = ex1(w, cur[(2 * i + 1) >> 4][(2 * i + 1) & 15]);
+    cur[(2 * i) >> 4][(2 * i) & 15] = ex1<kPre>(w, cur[(2 * i) >> 4][(2 * i) & 15]);
+    cur[(2 * i + 1) >> 4][(2 * i + 1) & 15] = ex1<kPre>(w, cur[(2 * i + 1) >> 4][(2 * i + 1) & 15]);
     if (i >= 4) {
       cv_op((i - 4) >> 2, 2 * ((i - 4) & 3));
       cv_op((i - 4) >> 2, 2 * ((i - 4) & 3) + 1);
@@ -420,8 +438,6 @@ attn_fwd_kernel(AttnArgs a) {
   const bool row_valid = row < a.n_valid;
 
   load_q_operands<kFusedQ>(a, row, head, hl, &ft, w.q);
-  w.c = c2;
-  w.tau = kTauP / c2;
   w.m = 0.0f;
   w.nmc = 0.0f;
   w.mt = 0.0f;
@@ -433,6 +449,15 @@ attn_fwd_kernel(AttnArgs a) {
   const char* img = a.img + (int64_t)head * a.tiles_per_head * kTileImageBytes;
   const int tail = (int)(a.n_valid - (int64_t)(nt - 1) * kTileKeys);  // valid keys, last tile
 
+  // The factor the stored K rows carry (tile 0's pad; the same for every tile).  When it
+  // is c2 itself, the scores leave the matrix cores in exp2 units: the QK accumulation
+  // then starts at -m and p = exp2(score), with no per-score multiply-add (kPre).
+  const float kmul = __int_as_float(
+      __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(img + kKMulOffset)));
+  const bool prescaled = kmul == c2;
+  w.c = prescaled ? 1.0f : c2 / kmul;
+  w.tau = kTauP / w.c;
+
   // Tiles go straight from global memory into their LDS slot (global_load_lds_dwordx4:
   // lane i of a wave writes 16 bytes at the wave's LDS base + 16 i).  Wave w copies the
   // 1 KiB chunks w, w + 8, ... of the 35 KiB image.
@@ -443,6 +468,7 @@ attn_fwd_kernel(AttnArgs a) {
     return (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(smem_addr + ((unsigned)t % (unsigned)kSlots) * (unsigned)kTileImageBytes));
   };
+  const uint32_t lane_off = lane * 16;
   auto load = [&](int t) __attribute__((always_inline)) {
     const char* src = img + (int64_t)t * kTileImageBytes;
     char* dst = slot(t);
@@ -450,7 +476,7 @@ attn_fwd_kernel(AttnArgs a) {
     for (int i = 0; i < (kImageChunks + kWaves - 1) / kWaves; ++i) {
       const int c = wave + i * kWaves;
       if (c < kImageChunks)
-        dma_to_lds16(src + c * 1024 + lane * 16,
+        dma_to_lds16(src + c * 1024, lane_off,
                      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(dst + c * 1024));
     }
   };
@@ -481,14 +507,16 @@ attn_fwd_kernel(AttnArgs a) {
   // choices are compile-time so that no branch separates the products from the work
   // they overlap.
   auto step = [&](f32x16* cur, f32x16* nxt, int j, auto next_tag, auto mask_tag,
-                  auto check_tag) __attribute__((always_inline)) {
+                  auto check_tag, auto pre_tag) __attribute__((always_inline)) {
     constexpr bool kNext = decltype(next_tag)::value;
     constexpr bool kMask = decltype(mask_tag)::value;
     constexpr bool kChk = decltype(check_tag)::value;
+    constexpr bool kPre = decltype(pre_tag)::value;
+    static_assert(!(kChk && kPre), "the running max is never raised with prescaled K");
     if (j + kSlots - 1 < nt) load(j + kSlots - 1);  // into the slot tile j-1 left
     if (kNext) {
       float v;
-      steady_step<kChk>(w, cur, nxt, slot_addr(j + 1) + k_lane, slot_addr(j) + v_lane, v);
+      steady_step<kChk, kPre>(w, cur, nxt, slot_addr(j + 1) + k_lane, slot_addr(j) + v_lane, v);
       if (kMask) {
         mask_tail(nxt);
         if (kChk) {  // the max taken in the step saw the masked keys: take it again
@@ -501,7 +529,7 @@ attn_fwd_kernel(AttnArgs a) {
       }
       if (kChk) mx_finish(w, v);
     } else {  // last tile: no next scores
-      ex(w, cur);
+      ex<kPre>(w, cur);
       cv(w, cur);
       pv(w, slot_addr(j) + v_lane);
     }
@@ -533,7 +561,7 @@ attn_fwd_kernel(AttnArgs a) {
   if (!kCheck) {
     const float kmax = head_kmax(img, nt, lane);
     const float bound = sqrtf(q_norm2(w.q)) * 1.0001f * kmax;
-    const bool ok = (bound - w.m) * c2 <= 64.0f;  // false for NaN as well
+    const bool ok = (bound - w.m) * w.c <= 64.0f;  // false for NaN as well
     __shared__ int wave_fail[kWaves];
     if (lane == 0) wave_fail[wave] = __builtin_amdgcn_ballot_w64(!ok) != 0;
     __syncthreads();
@@ -549,23 +577,39 @@ attn_fwd_kernel(AttnArgs a) {
   // The score sets alternate sa -> sb -> sa; for every path to reach the loop with the
   // current tile in sa and leave it with the same, an odd count of steady steps peels
   // one first.
+  // kPre: the tile-0 scores are first made relative to the running max.
   using Check = std::integral_constant<bool, kCheck>;
-  if (nt == 1) {
-    step(sa, sb, 0, F{}, F{}, Check{});
+  auto steps = [&](auto pre_tag) __attribute__((always_inline)) {
+    using Pre = decltype(pre_tag);
+    if (Pre::value) shift_scores(w, sa, w.m);
+    if (nt == 1) {
+      step(sa, sb, 0, F{}, F{}, Check{}, Pre{});
+    } else {
+      int j = 0;
+      if (nt & 1) {
+        step(sa, sb, 0, T{}, F{}, Check{}, Pre{});
+        sa[0] = sb[0];
+        sa[1] = sb[1];
+        j = 1;
+      }
+      for (; j < nt - 2; j += 2) {
+        step(sa, sb, j, T{}, F{}, Check{}, Pre{});
+        step(sb, sa, j + 1, T{}, F{}, Check{}, Pre{});
+      }
+      step(sa, sb, nt - 2, T{}, T{}, Check{}, Pre{});
+      step(sb, sa, nt - 1, F{}, F{}, Check{}, Pre{});
+    }
+  };
+  // The checked pass takes the multiply-add path for either kind of K (c = 1 for
+  // prescaled K): the rare raise of the running max needs registers the kPre path
+  // would spill.
+  if constexpr (!kCheck) {
+    if (prescaled)
+      steps(T{});
+    else
+      steps(F{});
   } else {
-    int j = 0;
-    if (nt & 1) {
-      step(sa, sb, 0, T{}, F{}, Check{});
-      sa[0] = sb[0];
-      sa[1] = sb[1];
-      j = 1;
-    }
-    for (; j < nt - 2; j += 2) {
-      step(sa, sb, j, T{}, F{}, Check{});
-      step(sb, sa, j + 1, T{}, F{}, Check{});
-    }
-    step(sa, sb, nt - 2, T{}, T{}, Check{});
-    step(sb, sa, nt - 1, F{}, F{}, Check{});
+    steps(F{});
   }
 
   // ---- epilogue: lane holds O[row][d = db*32 + 8i + 4hl + j] at register 4i+j

@@ -404,13 +404,14 @@ attn_fp8_kernel(Fp8AttnArgs a) {
   auto slot = [&](int t) __attribute__((always_inline)) {
     return smem + ((unsigned)t % (unsigned)kSlots) * (unsigned)kTileBytes;
   };
+  const uint32_t lane_off = lane * 16;
   auto load = [&](int t) __attribute__((always_inline)) {
     const char* src = img + (int64_t)t * kTileBytes;
     const uint32_t dst = slot_addr(t);
 #pragma unroll
     for (int i = 0; i < (kImgChunks + kWaves - 1) / kWaves; ++i) {
       const int c = wave + i * kWaves;
-      if (c < kImgChunks) dma_to_lds16(src + c * 1024 + lane * 16, dst + c * 1024);
+      if (c < kImgChunks) dma_to_lds16(src + c * 1024, lane_off, dst + c * 1024);
     }
   };
   auto loads_done = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };

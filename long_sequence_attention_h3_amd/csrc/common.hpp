@@ -30,8 +30,10 @@ constexpr int kKImageBytes = kTileKeys * kKRowPitch;      // 17,408
 constexpr int kVImageBytes = kHeadDim * kVRowPitch;       // 18,432
 constexpr int kTileImageBytes = kKImageBytes + kVImageBytes;  // 35,840 = 35 KiB
 // The pad of K row 0 carries the tile's largest K row norm (fp32, the norm of the bf16
-// values stored), the rest of every pad is zero.
-constexpr int kKNormOffset = kHeadDim * 2;  // byte 256 of the image
+// values stored) and then the fp32 factor the stored K rows were multiplied by before
+// rounding (1: stored as given); the rest of every pad is zero.
+constexpr int kKNormOffset = kHeadDim * 2;      // byte 256 of the image
+constexpr int kKMulOffset = kKNormOffset + 4;   // byte 260
 
 // Rotary descriptor as the kernels see it.
 struct RopeArgs {
@@ -87,7 +89,11 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // Copy 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
-// lane i's 16 bytes at `src` (its own address) land at LDS byte lds_base + 16 i.
+// lane i's 16 bytes at sbase + voff (voff its own) land at LDS byte lds_base + 16 i.
+// The scalar-base form of the instruction takes the wave-uniform sbase in SGPRs and a
+// 32-bit per-lane offset, so a copy costs no per-lane address arithmetic (with a 64-bit
+// per-lane address the copies cost 64-bit vector adds in the attention loops, measured
+// at 2 % of the bf16 kernel's time).
 // Issued as inline assembly on purpose: the compiler cannot tell which LDS bytes the
 // copy writes, and for the intrinsic it conservatively waits for every outstanding copy
 // before the next LDS read; the callers instead wait for their own copies explicitly
@@ -96,12 +102,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 // other code in this library uses M0, so setting it here disturbs nothing.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_to_lds16(const void* src, uint32_t lds_base) {
+__device__ __forceinline__ void dma_to_lds16(const void* sbase, uint32_t voff,
+                                             uint32_t lds_base) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(src), "s"(lds_base)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
       : "memory", "m0");
 }
 #pragma clang diagnostic pop

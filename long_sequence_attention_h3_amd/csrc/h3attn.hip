@@ -163,16 +163,22 @@ h3_status check_norm(const void* w, int64_t w_head_stride, float eps, const h3_r
 }
 
 // ---------------------------------------------------------------- stage 1: K/V pack
+// The attention kernels' exp2 scale; the layer path also stores normalised K times it.
+float exp2_scale(float softmax_scale) { return softmax_scale * 1.4426950408889634f; }
+
 h3_status do_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
-                     float eps, const h3_rope* rope, const h3_shape* shp, void* workspace,
-                     size_t ws_bytes, hipStream_t stream) {
+                     float eps, const h3_rope* rope, float softmax_scale, const h3_shape* shp,
+                     void* workspace, size_t ws_bytes, hipStream_t stream) {
   int64_t max_valid = 0;
   H3_TRY(check_shape(shp, &max_valid));
   if (!k || !v) return H3_ERR_NULL;
   if (!aligned16(k) || !aligned16(v)) return H3_ERR_ALIGN;
   const bool norm = w_k != nullptr;
   RopeArgs ra{};
-  if (norm) H3_TRY(check_norm(w_k, w_head_stride, eps, rope, max_valid, &ra));
+  if (norm) {
+    H3_TRY(check_norm(w_k, w_head_stride, eps, rope, max_valid, &ra));
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  }
   H3_TRY(check_workspace(shp, workspace, ws_bytes));
   H3_TRY(check_device());
   const int64_t S = shp->seq_buf, tph = tiles_per_head(shp);
@@ -190,6 +196,7 @@ h3_status do_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_he
     pa.n_valid = n;
     pa.tiles_per_head = tph;
     pa.eps = eps;
+    pa.k_mul = norm ? exp2_scale(softmax_scale) : 1.0f;
     pa.rope = ra;
     pa.img = ws;
     const dim3 grid((unsigned)((n + kTileKeys - 1) / kTileKeys), (unsigned)shp->num_heads);
@@ -237,7 +244,7 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
     aa.seq_buf = S;
     aa.heads = H;
     aa.m_tiles = m_tiles;
-    aa.scale_log2 = softmax_scale * 1.4426950408889634f;
+    aa.scale_log2 = exp2_scale(softmax_scale);
     aa.w_q = static_cast<const __bf16*>(w_q);
     aa.w_head_stride = w_head_stride;
     aa.eps = eps;
@@ -351,7 +358,7 @@ h3_status do_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_
     aa.seq_buf = S;
     aa.heads = H;
     aa.m_tiles = m_tiles;
-    aa.scale_log2 = softmax_scale * 1.4426950408889634f;
+    aa.scale_log2 = exp2_scale(softmax_scale);
     aa.w_q = static_cast<const __bf16*>(w_q);
     aa.w_head_stride = w_head_stride;
     aa.eps = eps;
@@ -437,10 +444,10 @@ size_t h3_attn_workspace_size(const h3_shape* shape) {
 }
 
 h3_status h3_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
-                     float eps, const h3_rope* rope, const h3_shape* shape, void* workspace,
-                     size_t workspace_bytes_, hipStream_t stream) {
-  return do_kv_pack(k, v, w_k, w_head_stride, eps, rope, shape, workspace, workspace_bytes_,
-                    stream);
+                     float eps, const h3_rope* rope, float softmax_scale, const h3_shape* shape,
+                     void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+  return do_kv_pack(k, v, w_k, w_head_stride, eps, rope, softmax_scale, shape, workspace,
+                    workspace_bytes_, stream);
 }
 
 h3_status h3_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head_stride,
@@ -458,8 +465,8 @@ h3_status h3_attn_varlen(const void* q, const void* k, const void* v, void* o,
   if (!q || !o) return H3_ERR_NULL;
   if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
-  H3_TRY(do_kv_pack(k, v, nullptr, 0, 0.0f, nullptr, shape, workspace, workspace_bytes_,
-                    stream));
+  H3_TRY(do_kv_pack(k, v, nullptr, 0, 0.0f, nullptr, softmax_scale, shape, workspace,
+                    workspace_bytes_, stream));
   return do_attn_packed(q, o, nullptr, 0, 0.0f, nullptr, softmax_scale, shape, workspace,
                         workspace_bytes_, stream);
 }
@@ -472,8 +479,8 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
   if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
   if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
   H3_TRY(check_weights(w_q, w_k, w_head_stride));
-  H3_TRY(do_kv_pack(k, v, w_k, w_head_stride, eps, rope, shape, workspace, workspace_bytes_,
-                    stream));
+  H3_TRY(do_kv_pack(k, v, w_k, w_head_stride, eps, rope, softmax_scale, shape, workspace,
+                    workspace_bytes_, stream));
   return do_attn_packed(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape, workspace,
                         workspace_bytes_, stream);
 }

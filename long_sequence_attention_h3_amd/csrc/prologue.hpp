@@ -218,11 +218,14 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
 //   V part: channel d, key chunk c at byte 17408 + d*144 + 16c, where chunk c holds, in
 //           order, the keys 16(c/2) + 4(c%2) + {0,1,2,3} and 16(c/2) + 8 + 4(c%2) + {0,1,2,3}.
 // The pad after K row 0 holds the tile's largest K row norm (the attention kernel bounds
-// its scores with it).
+// its scores with it) and the factor k_mul.  With `norm` set, K rows are RMS-normalised
+// and rotated on the way (the layer path) and multiplied by k_mul in fp32 before their
+// one rounding to bf16: the attention kernel passes softmax_scale * log2(e), so its
+// scores come out of the matrix cores in exp2 units.  Without `norm`, K is copied as
+// given and k_mul is 1 (scaling bf16 input would round it a second time).
 // The V key order inside each 16-key group (bits 2 and 3 of the key index exchanged)
 // is the order in which the QK product leaves the probabilities in registers, so the PV
-// product consumes them without shuffles.  Keys >= N are written as zeros.  With `norm`
-// set, K rows are RMS-normalised and rotated on the way (the layer path).
+// product consumes them without shuffles.  Keys >= N are written as zeros.
 struct PackArgs {
   const __bf16* k;
   const __bf16* v;
@@ -232,6 +235,7 @@ struct PackArgs {
   int64_t n_valid;
   int64_t tiles_per_head;  // capacity of the image array per head
   float eps;
+  float k_mul;             // applied to normalised K rows before rounding (1 without norm)
   RopeArgs rope;
   char* img;               // [head][tile] x kTileImageBytes
 };
@@ -263,6 +267,8 @@ __global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
         const ChunkRot cr = chunk_rotation(a.rope, key, cc);
         float y[8];
         norm_rotate_row16(row, a.w_k + (int64_t)h * a.w_head_stride, a.eps, cr, cc, &ft, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= a.k_mul;
         out = pack8(y);
       } else {
         out = *reinterpret_cast<const u32x4*>(row + cc * 8);
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
   if (cc == 0) row_max[tid >> 4] = norm2_max;
   __syncthreads();
   // the K row pads: row 0's carries the tile's largest row norm (rounded up a little so
-  // that it bounds the fp32 norm of every row), the others are zero
+  // that it bounds the fp32 norm of every row) and k_mul, the others are zero
   if (tid < kTileKeys) {
     u32x4 pad = {0u, 0u, 0u, 0u};
     if (tid == 0) {
@@ -290,6 +296,7 @@ __global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
 #pragma unroll
       for (int i = 1; i < 8; ++i) m2 = fmaxf(m2, row_max[i]);
       pad[0] = __float_as_uint(sqrtf(m2) * 1.0001f);
+      pad[1] = __float_as_uint(kNorm ? a.k_mul : 1.0f);
     }
     *reinterpret_cast<u32x4*>(img + tid * kKRowPitch + kKNormOffset) = pad;
   }

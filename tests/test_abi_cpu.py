@@ -133,9 +133,15 @@ def test_stage_entry_points_validate():
     s = shape()
     need = L.h3_attn_workspace_size(ctypes.byref(s))
     r = rope()
-    assert L.h3_kv_pack(0, FAKE, None, 0, 0.0, None, ctypes.byref(s), WS, need, None) == 1
-    assert L.h3_kv_pack(FAKE, FAKE, None, 0, 0.0, None, ctypes.byref(s), WS, need - 1, None) == 7
-    assert L.h3_kv_pack(FAKE, FAKE, FAKE, 0, 1e-6, None, ctypes.byref(s), WS, need, None) == 1
+    assert L.h3_kv_pack(0, FAKE, None, 0, 0.0, None, 0.0, ctypes.byref(s), WS, need, None) == 1
+    assert L.h3_kv_pack(FAKE, FAKE, None, 0, 0.0, None, 0.0, ctypes.byref(s), WS, need - 1,
+                        None) == 7
+    assert L.h3_kv_pack(FAKE, FAKE, FAKE, 0, 1e-6, None, 0.1, ctypes.byref(s), WS, need,
+                        None) == 1
+    # with w_k the softmax scale (the stored K's multiplier) must be positive and finite
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert L.h3_kv_pack(FAKE, FAKE, FAKE, 0, 1e-6, ctypes.byref(r), bad, ctypes.byref(s),
+                            WS, need, None) == 2
     assert L.h3_attn_packed(FAKE, 0, None, 0, 0.0, None, 0.1, ctypes.byref(s), WS, need,
                             None) == 1
     assert L.h3_attn_packed(FAKE, FAKE, FAKE, 0, 1e-6, ctypes.byref(rope(n_1d=10)), 0.1,
@@ -153,7 +159,10 @@ def test_valid_call_without_device_fails_loudly():
     assert layer(s, rope()) == 5
     assert prologue(s, rope()) == 5
     need = L.h3_attn_workspace_size(ctypes.byref(s))
-    assert L.h3_kv_pack(FAKE, FAKE, None, 0, 0.0, None, ctypes.byref(s), WS, need, None) == 5
+    assert L.h3_kv_pack(FAKE, FAKE, None, 0, 0.0, None, 0.0, ctypes.byref(s), WS, need,
+                        None) == 5
+    assert L.h3_kv_pack(FAKE, FAKE, FAKE, 0, 1e-6, ctypes.byref(rope()), 0.1, ctypes.byref(s),
+                        WS, need, None) == 5
     assert L.h3_attn_packed(FAKE, FAKE, None, 0, 0.0, None, 0.1, ctypes.byref(s), WS, need,
                             None) == 5
 

@@ -117,7 +117,9 @@ def test_large_scores_mix_both_passes(dev):
     every row against the oracle.  The layer variant scales head 1's w_q by 8: logits
     that large magnify the unavoidable bf16 rounding of the normalised Q and K that the
     matrix cores consume (about 2^-9 relative per element), so that variant is checked
-    against the oracle's fp64 prologue rounded to bf16, then the oracle's attention."""
+    against the oracle's fp64 prologue rounded as the layer rounds it (Q to bf16; K times
+    c = softmax_scale * log2(e) in fp32, then to bf16), then the oracle's attention with
+    the scale divided by c."""
     from oracle import oracle as O
     n, s = 1500, 1536
     w = small(n, s, heads=2, seed=57)
@@ -148,15 +150,16 @@ def test_large_scores_mix_both_passes(dev):
     torch.cuda.synchronize()
     rope = O.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
 
-    def normed_bf16(x, wt):  # [S, H, D] bf16 bits: oracle prologue, rounded to bf16
+    def normed_bf16(x, wt, mul=1.0):  # [S, H, D] bf16: oracle prologue times mul, rounded
         y = O.prologue(W.bits(x), n, W.bits(wt), w.eps, rope, np.arange(n), w_head_stride=128)
         full = torch.zeros((s, 2, 128), dtype=torch.bfloat16)
-        full[:n] = torch.from_numpy(y).to(torch.float32).to(torch.bfloat16)
+        full[:n] = (torch.from_numpy(y).to(torch.float32) * mul).to(torch.bfloat16)
         return full
 
+    c = float(np.float32(scale_of(w)) * np.float32(1.4426950408889634))
     ref = O.attn_varlen(W.bits(normed_bf16(inp["q"][0], wq)),
-                        W.bits(normed_bf16(inp["k"][0], wk)), W.bits(inp["v"][0]), n,
-                        scale_of(w), np.asarray(rows))
+                        W.bits(normed_bf16(inp["k"][0], wk, c)), W.bits(inp["v"][0]), n,
+                        scale_of(w) / c, np.asarray(rows))
     assert_close(rows_of(out, rows), ref, "large scores layer")
 
 

@@ -21,7 +21,8 @@ from long_sequence_attention_h3_amd import workloads as W
 from oracle import oracle as O
 
 from parity_helpers import (assert_close, assert_tail_zero, gpu_layer, gpu_rope, gpu_varlen,
-                            oracle_layer, oracle_rope, oracle_varlen, rows_of, say, to_dev)
+                            oracle_layer, oracle_rope, oracle_varlen, rows_of, say, scale_of,
+                            to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,8 +115,29 @@ def test_prologue_in_place(dev):
 
 
 @pytest.mark.parametrize("cfg", [0, 4])
-def test_layer_equals_prologue_then_varlen_bitwise(cfg, dev):
-    """The fused layer and the two-call path round Q and K to bf16 identically."""
+def test_fused_q_prologue_bitwise(cfg, dev):
+    """The Q rows the layer normalises and rotates in registers are bit for bit the ones
+    h3_qk_rmsnorm_rope writes: the layer equals h3_kv_pack (fused K) followed by
+    h3_attn_packed of the standalone prologue's Q (no fused Q)."""
+    w = W.WORKLOADS[cfg]
+    inp = inputs(cfg)
+    d = to_dev(inp, dev)
+    say(f"[layer vs prologue Q + packed] workload {cfg}")
+    fused = gpu_layer(w, d)
+    n = inp["n_valid"]
+    q2, _ = B.qk_rmsnorm_rope(d["q"], d["k"], d["w_q"], d["w_k"], n, w.eps, gpu_rope(w))
+    ws = B.kv_pack(d["k"], d["v"], n, w_k=d["w_k"], eps=w.eps, rope=gpu_rope(w),
+                   softmax_scale=scale_of(w))
+    two = B.attn_packed(q2, ws, n, scale_of(w))
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), two.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_layer_close_to_prologue_then_varlen(cfg, dev):
+    """The two-call path (bf16 K as h3_qk_rmsnorm_rope writes it, scaled in fp32 inside
+    attention) and the layer (K rounded once after scaling) differ only by the rounding
+    of K: both within the bar of the oracle, and within 4e-3 of each other."""
     w = W.WORKLOADS[cfg]
     inp = inputs(cfg)
     d = to_dev(inp, dev)
@@ -123,9 +145,12 @@ def test_layer_equals_prologue_then_varlen_bitwise(cfg, dev):
     fused = gpu_layer(w, d)
     q2, k2 = B.qk_rmsnorm_rope(d["q"], d["k"], d["w_q"], d["w_k"], inp["n_valid"], w.eps,
                                gpu_rope(w))
-    d2 = dict(d, q=q2, k=k2)
-    two = gpu_varlen(w, d2)
-    assert torch.equal(fused.view(torch.int16), two.view(torch.int16))
+    two = gpu_varlen(w, dict(d, q=q2, k=k2))
+    n = w.n_valid
+    diff = (fused[0, :n].float() - two[0, :n].float()).abs()
+    say(f"  max|d| {diff.max().item():.3e} mean|d| {diff.mean().item():.3e}")
+    assert diff.max().item() <= 4e-3
+    assert torch.equal(fused[0, n:], two[0, n:])
 
 
 @pytest.mark.parametrize("cfg", [0, 1])
