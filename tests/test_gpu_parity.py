@@ -133,6 +133,25 @@ def test_fused_q_prologue_bitwise(cfg, dev):
     assert torch.equal(fused.view(torch.int16), two.view(torch.int16))
 
 
+@pytest.mark.parametrize("cfg", [0, 4])
+def test_unscaled_k_with_fused_q_bitwise(cfg, dev):
+    """K tiles packed as given (h3_kv_pack without w_k, from the standalone prologue's K)
+    with the fused Q prologue (h3_attn_packed with w_q) equal h3_attn_varlen of the
+    standalone prologue's Q and K bit for bit: the attention kernel reads the tiles'
+    K factor and takes the multiply-add form for them."""
+    w = W.WORKLOADS[cfg]
+    inp = inputs(cfg)
+    d = to_dev(inp, dev)
+    say(f"[unscaled K + fused Q vs prologue+varlen] workload {cfg}")
+    n = inp["n_valid"]
+    q2, k2 = B.qk_rmsnorm_rope(d["q"], d["k"], d["w_q"], d["w_k"], n, w.eps, gpu_rope(w))
+    ws = B.kv_pack(k2, d["v"], n)
+    mixed = B.attn_packed(d["q"], ws, n, scale_of(w), w_q=d["w_q"], eps=w.eps, rope=gpu_rope(w))
+    two = gpu_varlen(w, dict(d, q=q2, k=k2))
+    torch.cuda.synchronize()
+    assert torch.equal(mixed.view(torch.int16), two.view(torch.int16))
+
+
 @pytest.mark.parametrize("cfg", [0, 1])
 def test_layer_close_to_prologue_then_varlen(cfg, dev):
     """The two-call path (bf16 K as h3_qk_rmsnorm_rope writes it, scaled in fp32 inside
