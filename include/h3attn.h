@@ -119,7 +119,8 @@ size_t h3_attn_workspace_size(const h3_shape* shape);
  * tiles as the attention kernel reads them; keys >= N_b stored as zeros).  With w_k
  * non-NULL each K row is first RMS-normalised (weights w_k, w_head_stride, eps) and
  * rotated (rope) with the arithmetic of h3_qk_rmsnorm_rope, then multiplied in fp32 by
- * softmax_scale * log2(e) and rounded once to bf16, so that the attention kernel's
+ * c = softmax_scale * log2(e) (when 2^-32 <= c <= 2^32; otherwise by 1, so that K
+ * stays in bf16's normal range) and rounded once to bf16, so that the attention kernel's
  * scores come out of the matrix cores in exp2 units (the layer's K operand is thus
  * bf16(k * softmax_scale * log2 e) rather than bf16(k): the same relative rounding,
  * of a different value).  With w_k NULL, K is stored as given and rope, eps and

@@ -166,6 +166,15 @@ h3_status check_norm(const void* w, int64_t w_head_stride, float eps, const h3_r
 // The attention kernels' exp2 scale; the layer path also stores normalised K times it.
 float exp2_scale(float softmax_scale) { return softmax_scale * 1.4426950408889634f; }
 
+// Factor for normalised K rows: the exp2 scale, unless it is so small or large that K
+// times it could leave bf16's normal range; then 1 (K stored as given), and the
+// attention kernel applies the scale per score instead (it reads the factor from the
+// tiles).
+float prescale_factor(float softmax_scale) {
+  const float c = exp2_scale(softmax_scale);
+  return (c >= 0x1p-32f && c <= 0x1p32f) ? c : 1.0f;
+}
+
 h3_status do_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_head_stride,
                      float eps, const h3_rope* rope, float softmax_scale, const h3_shape* shp,
                      void* workspace, size_t ws_bytes, hipStream_t stream) {
@@ -196,7 +205,7 @@ h3_status do_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_he
     pa.n_valid = n;
     pa.tiles_per_head = tph;
     pa.eps = eps;
-    pa.k_mul = norm ? exp2_scale(softmax_scale) : 1.0f;
+    pa.k_mul = norm ? prescale_factor(softmax_scale) : 1.0f;
     pa.rope = ra;
     pa.img = ws;
     const dim3 grid((unsigned)((n + kTileKeys - 1) / kTileKeys), (unsigned)shp->num_heads);

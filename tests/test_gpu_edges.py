@@ -90,6 +90,36 @@ def test_fused_qkv_buffer_row_stride(dev):
     assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16))
 
 
+@pytest.mark.parametrize("scale", [None, 1e-11])
+def test_layer_k_factor_and_extreme_scale(scale, dev):
+    """The K tiles record the factor the layer stored K with: softmax_scale * log2(e)
+    for ordinary scales, 1 when that factor would be below 2^-32 (K is then stored as
+    given and the kernel applies the scale per score).  Either way the layer matches
+    the oracle; at 1e-11 every score is ~0 and each row is the mean of V."""
+    import struct
+
+    from oracle import oracle as O
+    from parity_helpers import oracle_rope
+    w = small(700, 768, heads=2, seed=58)
+    sc = scale_of(w) if scale is None else scale
+    inp = W.generate(w, tail="nan")
+    d = to_dev(inp, dev)
+    say(f"[edge] layer K factor, softmax_scale {sc}")
+    ws = torch.empty(B.workspace_size(d["q"]), dtype=torch.uint8, device=dev)
+    out = B.attn_layer(d["q"], d["k"], d["v"], d["w_q"], d["w_k"], 700, w.eps, gpu_rope(w),
+                       sc, workspace=ws)
+    torch.cuda.synchronize()
+    factor = struct.unpack("<f", bytes(ws[260:264].cpu().tolist()))[0]
+    c = float(np.float32(sc) * np.float32(1.4426950408889634))
+    assert factor == (c if scale is None else 1.0), factor
+    rows = list(range(700))
+    ref = oracle_layer(w, inp, rows) if scale is None else O.attn_layer(
+        W.bits(inp["q"][0]), W.bits(inp["k"][0]), W.bits(inp["v"][0]), 700, W.bits(inp["w_q"]),
+        W.bits(inp["w_k"]), w.eps, oracle_rope(w), sc, np.asarray(rows))
+    assert_close(rows_of(out, rows), ref, f"layer scale {sc}")
+    assert_tail_zero(out, [700], "layer extreme scale")
+
+
 def test_per_head_norm_weights(dev):
     """w_head_stride = D: head h uses its own weights; checked against the oracle run
     head by head with that head's weights."""
