@@ -40,12 +40,16 @@ def test_ragged_lengths_match_oracle(n, s, dev):
         assert_close(rows_of(out, rows), orc(w, inp, rows), f"{entry} N={n} S={s}")
 
 
-def test_single_token_returns_its_value_exactly(dev):
+@pytest.mark.parametrize("entry", ["layer", "varlen"])
+def test_single_token_returns_its_value_exactly(entry, dev):
+    """N = 1: the one weight is exp2(0) = 1 in either form of the softmax (with prescaled
+    K the score minus its own maximum is exactly 0), so the output is v_0 bit for bit."""
     w = small(1, 80, heads=4, seed=51)
     inp = W.generate(w, tail="nan")
-    out = gpu_varlen(w, to_dev(inp, dev))
+    run = gpu_layer if entry == "layer" else gpu_varlen
+    out = run(w, to_dev(inp, dev))
     assert torch.equal(out[0, 0].cpu().view(torch.int16), inp["v"][0, 0].view(torch.int16))
-    assert_tail_zero(out, [1], "N=1")
+    assert_tail_zero(out, [1], f"{entry} N=1")
 
 
 @pytest.mark.parametrize("entry", ["layer", "varlen"])
