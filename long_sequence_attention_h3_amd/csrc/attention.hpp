@@ -45,7 +45,8 @@
 //  - K as given (bf16 input, where scaling would round it a second time): the
 //    accumulation starts at 0 and p = exp2(fma(s, c, -m c)), c applied in fp32.
 // The running max m is raised only when a score exceeds it by more than kTauP / c, so
-// p <= 2^8 and the O rescale is rare.  Keys >= N of the last tile get -inf scores.  P is rounded to bf16 for the PV product, and the row sums add exactly
+// p <= 2^8 and the O rescale is rare.  Keys >= N of the last tile get -inf scores.
+// P is rounded to bf16 for the PV product, and the row sums add exactly
 // those rounded values (v_dot2_f32_bf16 with (1, 1)), so every output row is a true
 // weighted average of V rows; summing the unrounded fp32 p instead costs up to 2^-9
 // relative error on strongly peaked rows.
