@@ -19,8 +19,11 @@ inputs already resident in HBM.  Prints one JSON line:
              inputs and on frame-local inputs of the same shape, with the share of wave
              tiles skipped and the dense bf16 / dense FP8 times on those inputs
   per_workload  every workload size: h3_attn_layer and h3_attn_varlen TFLOP/s (median and
-             min of 10 calls after 3 warm-up calls), the same for the FP8 calls, and
-             h3_qk_rmsnorm_rope GB/s
+             min of 10 calls after 3 warm-up calls), the same for the FP8 calls,
+             h3_qk_rmsnorm_rope GB/s, and (unless --no-cpu-baseline) `oracle`: the fp64
+             oracle timed on every row of the short workloads and on sampled rows of the
+             long ones (with the full-layer time extrapolated), checked against the
+             layer's output on those rows
   sclk_mhz   the shader clock the driver reported right after the timed region
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
@@ -123,19 +126,58 @@ def call_times(torch, stream, fn, warmup: int = 3, reps: int = 10):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
 
 
-def per_workload(torch, B, W, dev, stream):
-    """h3_attn_layer / h3_attn_varlen TFLOP/s and prologue GB/s on every workload size."""
+def oracle_check(W, w, inp, out_rows, rows, scale):
+    """The fp64 oracle of the layer on `rows` of every head, timed, against the GPU rows
+    `out_rows` ([R, H, D] float64): seconds, fp64 rate and the parity figures."""
+    import numpy as np
+    from oracle import oracle as O
+    threads = O.default_threads()
+    orope = O.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
+    t0 = time.perf_counter()
+    ref = O.attn_layer(W.bits(inp["q"][0]), W.bits(inp["k"][0]), W.bits(inp["v"][0]),
+                       w.n_valid, W.bits(inp["w_q"]), W.bits(inp["w_k"]), w.eps, orope, scale,
+                       np.asarray(rows, dtype=np.int64), threads=threads)
+    t_cpu = time.perf_counter() - t0
+    err = np.abs(out_rows - ref)
+    rel = float(np.linalg.norm(out_rows - ref) / np.linalg.norm(ref))
+    ok = bool(err.max() <= 1.5e-2 and err.mean() <= 2e-3 and rel <= 1e-2)
+    flops = 4.0 * len(rows) * w.n_valid * w.head_dim * w.heads
+    return {"rows_per_head": len(rows), "all_rows": len(rows) == w.n_valid,
+            "threads": threads, "seconds": round(t_cpu, 3),
+            "tflops_fp64": round(flops / t_cpu / 1e12, 6),
+            "extrapolated_full_layer_s": round(t_cpu * w.n_valid / len(rows), 2),
+            "max_abs": float(err.max()), "mean_abs": float(err.mean()), "rel_l2": rel,
+            "ok": ok}
+
+
+def per_workload(torch, B, W, dev, stream, oracle_rows=None):
+    """h3_attn_layer / h3_attn_varlen TFLOP/s and prologue GB/s on every workload size;
+    with `oracle_rows`, also the fp64 oracle timed on that many sampled rows per head
+    (every row of the workloads with at most 8,192 valid tokens) and checked against the
+    layer's output."""
     import statistics
     table = {}
     for idx, w in sorted(W.WORKLOADS.items()):
         inp = W.generate(w, tail="nan")
         d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
-        del inp
         rope = B.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
         scale = 1.0 / math.sqrt(w.head_dim)
         n = d["n_valid"]
         out = torch.empty_like(d["q"])
         ws = torch.empty(B.workspace_size(d["q"]), dtype=torch.uint8, device=dev)
+        orc = None
+        if oracle_rows is not None:
+            rows = (list(range(w.n_valid)) if w.n_valid <= 8192
+                    else W.sample_rows(w, oracle_rows, 40_000 + idx))
+            B.attn_layer(d["q"], d["k"], d["v"], d["w_q"], d["w_k"], n, w.eps, rope, scale,
+                         out=out, workspace=ws)
+            idx_t = torch.as_tensor(rows, dtype=torch.long, device=dev)
+            got = out[0].index_select(0, idx_t).double().cpu().numpy()
+            orc = oracle_check(W, w, inp, got, rows, scale)
+            log(f"[bench] {w.name}: oracle {orc['seconds']}s on {len(rows)} rows/head, "
+                f"max {orc['max_abs']:.2e} mean {orc['mean_abs']:.2e} relL2 "
+                f"{orc['rel_l2']:.2e} -> {'ok' if orc['ok'] else 'FAIL'}")
+        del inp
         ws8 = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
         q2, k2 = torch.empty_like(d["q"]), torch.empty_like(d["k"])
         row = {"heads": w.heads, "n_valid": w.n_valid, "seq_buf": w.seq_buf,
@@ -164,6 +206,8 @@ def per_workload(torch, B, W, dev, stream):
         nbytes = 2 * 2 * w.batch * w.n_valid * w.heads * w.head_dim * 2
         row["h3_qk_rmsnorm_rope"] = {"ms_median": round(med, 4), "bytes": nbytes,
                                      "GB/s": round(nbytes / med / 1e6, 1)}
+        if orc is not None:
+            row["oracle"] = orc
         table[w.name] = row
         log(f"[bench] {w.name}: layer {row['h3_attn_layer']['tflops_median']} TFLOP/s, varlen "
             f"{row['h3_attn_varlen']['tflops_median']} TFLOP/s, layer_fp8 "
@@ -193,6 +237,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-rows-per-head", type=int, default=4096)
+    ap.add_argument("--oracle-rows-per-head", type=int, default=256,
+                    help="sampled rows per head of the per-workload oracle check on the "
+                         "long workloads (the short ones are checked on every row)")
     ap.add_argument("--no-per-workload", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large-scores", action="store_true",
@@ -511,7 +558,9 @@ def main() -> int:
     if not args.no_per_workload:
         del d, out, ws, q2, k2, layer_out
         torch.cuda.empty_cache()
-        result["per_workload"] = per_workload(torch, B, W, dev, stream)
+        result["per_workload"] = per_workload(
+            torch, B, W, dev, stream,
+            None if args.no_cpu_baseline else args.oracle_rows_per_head)
     print(json.dumps(result), flush=True)
     return 0
 

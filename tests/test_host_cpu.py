@@ -48,3 +48,23 @@ def test_source_hash_covers_every_kernel_source():
     for rel in bench.FP8_KERNEL_SOURCES:
         assert os.path.exists(os.path.join(ROOT, rel)), rel
 
+
+
+def test_bench_oracle_check_gates_parity():
+    """bench.oracle_check: the oracle's own rows pass the bar exactly, an all-zero output
+    (which an N ~ 59k layer misses by only 2-3x on the absolute bounds) fails it."""
+    import numpy as np
+    from oracle import oracle as O
+    from long_sequence_attention_h3_amd import workloads as W
+    w = W.Workload("host_check_300of320", heads=2, n_valid=300, seq_buf=320, seed=9)
+    inp = W.generate(w, tail="nan")
+    rows = [0, 17, 299]
+    scale = 1.0 / 128 ** 0.5
+    ref = O.attn_layer(W.bits(inp["q"][0]), W.bits(inp["k"][0]), W.bits(inp["v"][0]), 300,
+                       W.bits(inp["w_q"]), W.bits(inp["w_k"]), w.eps,
+                       O.make_rope(w.theta, 300), scale, np.asarray(rows))
+    good = bench.oracle_check(W, w, inp, ref, rows, scale)
+    assert good["ok"] and good["max_abs"] == 0.0 and good["rows_per_head"] == 3
+    assert not good["all_rows"] and good["extrapolated_full_layer_s"] >= good["seconds"]
+    bad = bench.oracle_check(W, w, inp, np.zeros_like(ref), rows, scale)
+    assert not bad["ok"]
