@@ -144,12 +144,12 @@ __device__ __forceinline__ void norm_rotate_chunk(const float* x, const float* x
 
 // ---------------------------------------------------------------------------------
 // One (token, head) row handled by 16 consecutive lanes, lane `cc` owning chunk cc.
-// Loads, normalises, rotates and returns the lane's 8 output values.  `row` points at
-// the head's 128 inputs, `w` at the head's 128 weights.  All 16 lanes must be active.
-__device__ __forceinline__ void norm_rotate_row16(const __bf16* row, const __bf16* w,
-                                                  float eps, const ChunkRot& cr, int cc,
+// Normalises and rotates the row whose chunk cc the lane holds in `raw` and returns the
+// lane's 8 output values; `w` points at the head's 128 weights.  All 16 lanes must be
+// active.
+__device__ __forceinline__ void norm_rotate_raw16(const u32x4 raw, const __bf16* w, float eps,
+                                                  const ChunkRot& cr, int cc,
                                                   const FreqTable* ft, float* out) {
-  const u32x4 raw = *reinterpret_cast<const u32x4*>(row + cc * 8);
   float x[8];
   unpack8(raw, x);
   float ss = chunk_sumsq(x);
@@ -168,6 +168,13 @@ __device__ __forceinline__ void norm_rotate_row16(const __bf16* row, const __bf1
   unpack8(*reinterpret_cast<const u32x4*>(w + cc * 8), wv);
   unpack8(*reinterpret_cast<const u32x4*>(w + cr.partner * 8), wpv);
   norm_rotate_chunk(x, xp, wv, wpv, inv, cr, ft, out);
+}
+
+// The same, loading chunk cc of the row at `row` (the head's 128 inputs).
+__device__ __forceinline__ void norm_rotate_row16(const __bf16* row, const __bf16* w,
+                                                  float eps, const ChunkRot& cr, int cc,
+                                                  const FreqTable* ft, float* out) {
+  norm_rotate_raw16(*reinterpret_cast<const u32x4*>(row + cc * 8), w, eps, cr, cc, ft, out);
 }
 
 struct PrologueArgs {
@@ -254,24 +261,36 @@ __global__ __launch_bounds__(128) void kv_pack_kernel(PackArgs a) {
   char* img = a.img + ((int64_t)h * a.tiles_per_head + kt) * kTileImageBytes;
   const int64_t hoff = (int64_t)h * kHeadDim;
 
-  // K: 64 rows x 16 chunks; 8 rows per pass (16 lanes per row).
+  // K: 64 rows x 16 chunks; 8 rows per pass (16 lanes per row).  All 8 rows of a lane are
+  // loaded before the first image store: the compiler cannot tell the image from K, so
+  // with a load per iteration every load would wait for the previous row's store.
   const int cc = tid & 15;
   float norm2_max = 0.0f;  // largest squared row norm seen by this thread's row group
-  for (int r = tid >> 4; r < kTileKeys; r += 8) {
+  u32x4 kraw[kTileKeys / 8];
+#pragma unroll
+  for (int i = 0; i < kTileKeys / 8; ++i) {
+    const int64_t key = key0 + (tid >> 4) + 8 * i;
+    kraw[i] = key < a.n_valid
+                  ? *reinterpret_cast<const u32x4*>(a.k + key * a.in_stride + hoff + cc * 8)
+                  : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < kTileKeys / 8; ++i) {
+    const int r = (tid >> 4) + 8 * i;
     const int64_t key = key0 + r;
     u32x4 out = {0u, 0u, 0u, 0u};
     // the whole 16-lane row group takes the same branch (one key per group)
     if (key < a.n_valid) {
-      const __bf16* row = a.k + key * a.in_stride + hoff;
       if (kNorm) {
         const ChunkRot cr = chunk_rotation(a.rope, key, cc);
         float y[8];
-        norm_rotate_row16(row, a.w_k + (int64_t)h * a.w_head_stride, a.eps, cr, cc, &ft, y);
+        norm_rotate_raw16(kraw[i], a.w_k + (int64_t)h * a.w_head_stride, a.eps, cr, cc, &ft,
+                          y);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] *= a.k_mul;
         out = pack8(y);
       } else {
-        out = *reinterpret_cast<const u32x4*>(row + cc * 8);
+        out = kraw[i];
       }
     }
     *reinterpret_cast<u32x4*>(img + r * kKRowPitch + cc * 16) = out;
