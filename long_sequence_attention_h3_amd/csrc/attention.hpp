@@ -30,11 +30,11 @@
 // and row sums; PV: O^T += V^T P^T.  The scores of tiles j and j+1 live in two register
 // sets used alternately (loop unrolled by two).
 //
-// With prescaled K in the fast pass, the second wave of each SIMD (waves 4-7) runs the
-// same work in another order instead: per step its 32 MFMAs back to back (QK(j+1),
-// PV(j)), then E and C of tile j+1 as one VALU block, with a single score set.  Paired
-// with an interleaving wave, whose VALU work sits in its QK half, the two keep the
-// matrix pipe busier than two interleaving waves do.
+// In the fast pass the second wave of each SIMD (waves 4-7) runs the same work in
+// another order instead: per step its 32 MFMAs back to back (QK(j+1), PV(j)), then E and
+// C of tile j+1 as one VALU block, with a single score set.  Paired with an interleaving
+// wave, whose VALU work sits in its QK half, the two keep the matrix pipe busier than
+// two interleaving waves do.
 //
 // Arithmetic.  Scores are exact bf16 products summed in fp32.  Two forms, chosen per
 // launch from the factor the K tiles were stored with:
@@ -313,12 +313,12 @@ __device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
   vmax = v;
 }
 
-// MFMA-first form of a step (prescaled K, fast pass; see the kernel for which waves take
-// it): the step's 32 MFMAs back to back, QK(j+1) into s (kNext) then PV(j) with the P
-// operands of tile j, each operand read three MFMAs ahead; then (valu_block) the P
-// operands and row sums of the new scores.  One score set suffices: a tile's scores
-// become P operands before the next QK overwrites them.
-template <bool kNext>
+// MFMA-first form of a step (fast pass; see the kernel for which waves take it): the
+// step's 32 MFMAs back to back, QK(j+1) into s (kNext) then PV(j) with the P operands of
+// tile j, each operand read three MFMAs ahead; then (valu_block) the P operands and row
+// sums of the new scores.  One score set suffices: a tile's scores become P operands
+// before the next QK overwrites them.  kPre as in steady_step.
+template <bool kNext, bool kPre>
 __device__ __forceinline__ void mfma_block(Wave& w, f32x16* s, uint32_t kbase,
                                            uint32_t vbase) {
   constexpr int nq = kNext ? 16 : 0;
@@ -340,8 +340,8 @@ __device__ __forceinline__ void mfma_block(Wave& w, f32x16* s, uint32_t kbase,
   for (int i = 0; i < n; ++i) {
     if (i < nq) {
       const int kb = i & 1, ks = i >> 1;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], w.q[ks], ks == 0 ? w.nm : s[kb],
-                                                      0, 0, 0);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          op[i], w.q[ks], ks == 0 ? (kPre ? w.nm : f32x16{}) : s[kb], 0, 0, 0);
     } else {
       const int k = i - nq, t = k >> 2, db = k & 3;
       w.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], w.p[t], w.o[db], 0, 0, 0);
@@ -351,8 +351,9 @@ __device__ __forceinline__ void mfma_block(Wave& w, f32x16* s, uint32_t kbase,
   }
 }
 
+template <bool kPre>
 __device__ __forceinline__ void valu_block(Wave& w, f32x16* s) {
-  ex<true>(w, s);
+  ex<kPre>(w, s);
   cv(w, s);
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -657,42 +658,47 @@ attn_fwd_kernel(AttnArgs a) {
       step(sb, sa, nt - 1, F{}, F{}, Check{}, Pre{});
     }
   };
-  // MFMA-first steps (prescaled K, fast pass): per step the 32 MFMAs, then the VALU
-  // work of the new tile; exactly nt barriers, as in `steps`.
-  auto mfma_first_steps = [&]() __attribute__((always_inline)) {
-    shift_scores(w, sa, w.m);
+  // MFMA-first steps (fast pass): per step the 32 MFMAs, then the VALU work of the new
+  // tile; exactly nt barriers, as in `steps`.
+  auto mfma_first_steps = [&](auto pre_tag) __attribute__((always_inline)) {
+    constexpr bool kPre = decltype(pre_tag)::value;
+    if (kPre) shift_scores(w, sa, w.m);
     auto kaddr = [&](int t) __attribute__((always_inline)) { return slot_addr(t) + k_lane; };
     auto vaddr = [&](int t) __attribute__((always_inline)) { return slot_addr(t) + v_lane; };
     auto body = [&](int j, auto mask_tag) __attribute__((always_inline)) {
       if (j + kSlots - 1 < nt) load(j + kSlots - 1);
-      mfma_block<true>(w, sa, kaddr(j + 1), vaddr(j));
+      mfma_block<true, kPre>(w, sa, kaddr(j + 1), vaddr(j));
       if (decltype(mask_tag)::value) mask_tail(sa);
-      valu_block(w, sa);
+      valu_block<kPre>(w, sa);
       loads_done();
       __syncthreads();
     };
-    valu_block(w, sa);  // P operands of tile 0
+    valu_block<kPre>(w, sa);  // P operands of tile 0
     for (int j = 0; j < nt - 2; ++j) body(j, F{});
     if (nt >= 2) body(nt - 2, T{});
-    mfma_block<false>(w, sa, 0, vaddr(nt - 1));
+    mfma_block<false, kPre>(w, sa, 0, vaddr(nt - 1));
     loads_done();
     __syncthreads();
   };
-  // Prescaled K, fast pass: waves 0-3 take the interleaved steps and waves 4-7 the
-  // MFMA-first ones.  A workgroup's waves are placed on the SIMDs in turn, so waves w
-  // and w + 4 share a SIMD: while one runs the exp2 work that the interleaved form packs
-  // into its QK half, the other keeps the matrix pipe busy (1.1-1.3 % faster than both
-  // waves interleaved, in interleaved A/Bs; the same output bits).  The checked pass
-  // takes the multiply-add path for either kind of K (c = 1 for prescaled K): the rare
-  // raise of the running max needs registers the kPre path would spill.
+  // Fast pass: waves 0-3 take the interleaved steps and waves 4-7 the MFMA-first ones.
+  // A workgroup's waves are placed on the SIMDs in turn, so waves w and w + 4 share a
+  // SIMD: while one runs the exp2 work that the interleaved form packs into its QK half,
+  // the other keeps the matrix pipe busy (prescaled K: 1.1-1.3 % faster than both waves
+  // interleaved; the multiply-add form, with the copies from waves 0-3: 1.7 %; in
+  // interleaved A/Bs, the same output bits).  The checked pass takes the multiply-add
+  // path for either kind of K (c = 1 for prescaled K) with all waves interleaved: the
+  // rare raise of the running max needs registers the kPre path would spill.
   if constexpr (!kCheck) {
     if (prescaled) {
       if (wave >= kWaves / 2)
-        mfma_first_steps();
+        mfma_first_steps(T{});
       else
         steps(T{});
     } else {
-      steps(F{});
+      if (wave >= kWaves / 2)
+        mfma_first_steps(F{});
+      else
+        steps(F{});
     }
   } else {
     steps(F{});
