@@ -662,6 +662,7 @@ attn_fwd_kernel(AttnArgs a) {
   // tile; exactly nt barriers, as in `steps`.
   auto mfma_first_steps = [&](auto pre_tag) __attribute__((always_inline)) {
     constexpr bool kPre = decltype(pre_tag)::value;
+    static_assert(!(kCheck && kPre), "the running max is never raised with prescaled K");
     if (kPre) shift_scores(w, sa, w.m);
     auto kaddr = [&](int t) __attribute__((always_inline)) { return slot_addr(t) + k_lane; };
     auto vaddr = [&](int t) __attribute__((always_inline)) { return slot_addr(t) + v_lane; };
@@ -669,6 +670,14 @@ attn_fwd_kernel(AttnArgs a) {
       if (j + kSlots - 1 < nt) load(j + kSlots - 1);
       mfma_block<true, kPre>(w, sa, kaddr(j + 1), vaddr(j));
       if (decltype(mask_tag)::value) mask_tail(sa);
+      if (kCheck) {  // M of tile j+1 (the maximum is exact, so the order does not matter)
+        float v = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v = fmaxf(v, sa[kb][e]);
+        mx_finish(w, v);
+      }
       valu_block<kPre>(w, sa);
       loads_done();
       __syncthreads();
@@ -685,9 +694,9 @@ attn_fwd_kernel(AttnArgs a) {
   // SIMD: while one runs the exp2 work that the interleaved form packs into its QK half,
   // the other keeps the matrix pipe busy (prescaled K: 1.1-1.3 % faster than both waves
   // interleaved; the multiply-add form, with the copies from waves 0-3: 1.7 %; in
-  // interleaved A/Bs, the same output bits).  The checked pass takes the multiply-add
-  // path for either kind of K (c = 1 for prescaled K) with all waves interleaved: the
-  // rare raise of the running max needs registers the kPre path would spill.
+  // interleaved A/Bs, the same output bits).  The checked pass pairs its waves the same
+  // way and takes the multiply-add path for either kind of K (c = 1 for prescaled K):
+  // the rare raise of the running max needs registers the kPre path would spill.
   if constexpr (!kCheck) {
     if (prescaled) {
       if (wave >= kWaves / 2)
@@ -701,7 +710,10 @@ attn_fwd_kernel(AttnArgs a) {
         steps(F{});
     }
   } else {
-    steps(F{});
+    if (wave >= kWaves / 2)
+      mfma_first_steps(F{});
+    else
+      steps(F{});
   }
 
   // ---- epilogue: lane holds O[row][d = db*32 + 8i + 4hl + j] at register 4i+j
