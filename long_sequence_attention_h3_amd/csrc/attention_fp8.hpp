@@ -11,8 +11,9 @@
 //   Q: one scale per token, amax/448, applied in registers on load (after the fused
 //      RMSNorm + RoPE when it is on);  K: one scale per block of 16 keys ("K16"),
 //      computed by the pre-pass; V: one scale per channel over the valid tokens (a
-//      separate max pass); every quantization decision in fp32: x * (448/amax) clamped
-//      to +-448, then round to nearest even (v_cvt_pk_fp8_f32).
+//      separate max pass); every code is the E4M3 rounding (to nearest, ties to even) of
+//      the exact x * 448 / amax (see quant4 for why the arithmetic used decides it
+//      exactly).
 //   P: the weights of a streaming softmax: per 64-key tile t, with m_t the running row
 //      maximum of the scaled scores through tile t (log2 units, c = softmax_scale *
 //      log2(e) * sq * sk), P = E4M3(2^(8 + c s - m_t)) <= 256; O and the row sums are
@@ -60,9 +61,23 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHi);
 }
 
-// Four clamped fp32 values -> one dword of E4M3 codes (byte i = value i).
-__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
-  auto q = [&](float x) { return fminf(kMax, fmaxf(-kMax, x * inv)); };
+// Inverse of a group's scale for quant4: 448 / amax in fp64 (0 for an all-zero group).
+__device__ __forceinline__ double code_inverse(float amax) {
+  return amax > 0.0f ? 448.0 / (double)amax : 0.0;
+}
+
+// Four values of one group -> one dword of E4M3 codes (byte i = value i), each code the
+// rounding to nearest even of the exact t = x * 448 / amax.  x and amax are bf16 values
+// (at most 8 significant bits), so t is either exactly an E4M3 rounding midpoint or at
+// least 2^-14 of its magnitude away from every midpoint (with x = X 2^a, amax = A 2^b,
+// X and A odd and below 256, t - M 2^e is a multiple of 2^min(a-b+6, e) over A, and
+// M < 32 for any neighbouring midpoint M 2^e).  Formed as an fp64 product with the fp64
+// inverse (relative error below 2^-51) and rounded once to fp32 (2^-24): a midpoint, with
+// its 5 significant bits, comes back exactly and the conversion breaks the tie to even;
+// any other t stays on its side of every midpoint.  |t| <= 448, so no clamp is needed;
+// the conversion is exact on [-448, 448].
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, double inv) {
+  auto q = [&](float x) { return (float)((double)x * inv); };
   return cvt2<true>(q(c), q(d), cvt2<false>(q(a), q(b), 0u));
 }
 
@@ -205,7 +220,7 @@ __global__ __launch_bounds__(256) void kv_pack_fp8_kernel(Fp8PackArgs a) {
     for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(x[i]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    const float inv = m > 0.0f ? kMax / m : 0.0f;
+    const double inv = code_inverse(m);
     u32x4 q0, q1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -230,7 +245,7 @@ __global__ __launch_bounds__(256) void kv_pack_fp8_kernel(Fp8PackArgs a) {
   {
     const int d = tid >> 1, hh = tid & 1;
     const float amax = __uint_as_float(a.vamax[h * kHeadDim + d]);
-    const float inv = amax > 0.0f ? kMax / amax : 0.0f;
+    const double inv = code_inverse(amax);
     float x[32];
 #pragma unroll
     for (int b = 0; b < 32; ++b) {
@@ -368,7 +383,7 @@ attn_fp8_kernel(Fp8AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[ks][i]));
     amax = pair_max(amax);
-    const float inv = amax > 0.0f ? kMax / amax : 0.0f;
+    const double inv = code_inverse(amax);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll

@@ -119,22 +119,23 @@ double h3o_e4m3(double x);
 /* Nearest bf16 of x (ties to even), as bits. */
 uint16_t h3o_round_bf16(double x);
 
-/* Quantize n fp32 values with one scale amax/448, in fp32 like the kernel: codes[i] =
- * E4M3(clamp(x[i] * (448 / amax))) as values; *scale = amax / 448 (0 if all zero). */
+/* Quantize n values (bf16 values passed as fp32, so exact) with one scale: codes[i] =
+ * E4M3(x[i] * 448 / amax) as values, evaluated in fp64; *scale = amax / 448 (0 if all
+ * zero). */
 void h3o_quantize_group(const float* x, int64_t n, double* codes, double* scale);
 
 /* FP8 attention on bf16 buffers whose Q and K are already normalised and rotated
- * (same layouts and row semantics as h3o_attn_varlen); the weights P are quantized
- * against the running row maximum of tiles of p_tile keys; with skip_threshold > 0 a
- * tile whose maximum is below the running maximum by a factor under skip_threshold
- * is dropped for that row (Skip-Softmax).  allow (optional, shaped like out): per element,
- * the largest change of the output that P codes lying within the matrix cores' score
- * error of a rounding midpoint can cause (see h3_oracle_fp8.cpp). */
+ * (same layouts and row semantics as h3o_attn_varlen), fp64 throughout: Q quantized per
+ * token, K per 16-key block, V per channel; the weights P quantized against the running
+ * row maximum of tiles of p_tile keys; with skip_threshold > 0 a tile whose maximum is
+ * below the running maximum by a factor under skip_threshold is dropped for that row
+ * (Skip-Softmax).  wmax (optional, [n_rows][heads]): each row's largest normalised
+ * weight (0 for rows >= n_valid). */
 int h3o_attn_varlen_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         int64_t seq_buf, int64_t n_valid, int64_t heads, int64_t d,
                         int64_t row_stride, double scale, int64_t p_tile, double skip_threshold,
                         const int64_t* rows, int64_t n_rows, int threads, double* out,
-                        double* allow);
+                        double* wmax);
 
 /* The FP8 layer: prologue of Q and K (fp64, rounded to bf16), then h3o_attn_varlen_fp8. */
 int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t seq_buf,
@@ -142,7 +143,7 @@ int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        const uint16_t* w_q, const uint16_t* w_k, int64_t w_head_stride,
                        double eps, const h3o_rope* rope, double scale, int64_t p_tile,
                        double skip_threshold, const int64_t* rows, int64_t n_rows, int threads,
-                       double* out, double* allow);
+                       double* out, double* wmax);
 
 /* ---- DiT block steps around attention: see h3_oracle_block.cpp for the reading. */
 

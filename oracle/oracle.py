@@ -235,7 +235,7 @@ def round_bf16(x: float) -> int:
 
 
 def quantize_group(x) -> tuple[np.ndarray, float]:
-    """One-scale FP8 quantization of fp32 values (decision in fp32): (codes, scale)."""
+    """One-scale FP8 quantization of bf16-valued inputs, decided in fp64: (codes, scale)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     codes = np.empty(x.size, dtype=np.float64)
     scale = ctypes.c_double()
@@ -248,45 +248,45 @@ FP8_P_TILE = 64  # keys per tile of the streamed softmax weights
 
 def attn_varlen_fp8(q_bits, k_bits, v_bits, n_valid: int, scale: float, rows,
                     threads: int | None = None, p_tile: int = FP8_P_TILE,
-                    skip_threshold: float = 0.0, with_allowance: bool = False):
+                    skip_threshold: float = 0.0, with_wmax: bool = False):
     """FP8 attention over bf16 [S, H, D] buffers (Q/K already prepared) -> [R, H, D];
     P quantized against the running row maximum of ``p_tile``-key tiles; tiles below
     the running maximum by a factor under ``skip_threshold`` dropped per row.  With
-    ``with_allowance`` returns (out, allowance): the per-element change that P codes
-    within the matrix cores' score error of a rounding midpoint can cause."""
+    ``with_wmax`` returns (out, wmax): wmax [R, H] is each row's largest normalised
+    weight."""
     q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
     S, H, D = q.shape
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.empty((rows.size, H, D), dtype=np.float64)
-    allow = np.empty_like(out) if with_allowance else None
+    wmax = np.empty((rows.size, H), dtype=np.float64)
     _check(lib().h3o_attn_varlen_fp8(_ptr(q), _ptr(k), _ptr(v), S, int(n_valid), H, D, H * D,
                                      float(scale), int(p_tile), float(skip_threshold),
                                      _ptr(rows), rows.size,
-                                     threads or default_threads(), _ptr(out),
-                                     _ptr(allow) if allow is not None else None),
+                                     threads or default_threads(), _ptr(out), _ptr(wmax)),
            "attn_varlen_fp8")
-    return (out, allow) if with_allowance else out
+    return (out, wmax) if with_wmax else out
 
 
 def attn_layer_fp8(q_bits, k_bits, v_bits, n_valid: int, wq_bits, wk_bits, eps: float,
                    rope: Rope, scale: float, rows, w_head_stride: int = 0,
                    threads: int | None = None, p_tile: int = FP8_P_TILE,
-                   skip_threshold: float = 0.0, with_allowance: bool = False):
-    """RMSNorm + RoPE (rounded to bf16) + FP8 attention over bf16 [S, H, D] buffers."""
+                   skip_threshold: float = 0.0, with_wmax: bool = False):
+    """RMSNorm + RoPE (rounded to bf16) + FP8 attention over bf16 [S, H, D] buffers;
+    ``with_wmax`` as for attn_varlen_fp8."""
     q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
     wq, wk = _u16(wq_bits), _u16(wk_bits)
     S, H, D = q.shape
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.empty((rows.size, H, D), dtype=np.float64)
-    allow = np.empty_like(out) if with_allowance else None
+    wmax = np.empty((rows.size, H), dtype=np.float64)
     _check(lib().h3o_attn_layer_fp8(_ptr(q), _ptr(k), _ptr(v), S, int(n_valid), H, D, H * D,
                                     _ptr(wq), _ptr(wk), int(w_head_stride), float(eps),
                                     ctypes.byref(rope), float(scale), int(p_tile),
                                     float(skip_threshold), _ptr(rows),
                                     rows.size, threads or default_threads(), _ptr(out),
-                                    _ptr(allow) if allow is not None else None),
+                                    _ptr(wmax)),
            "attn_layer_fp8")
-    return (out, allow) if with_allowance else out
+    return (out, wmax) if with_wmax else out
 
 
 def residual_norm_modulate(x, a_bits, gate, shift, scale, n_valid: int, eps: float):

@@ -4,11 +4,14 @@ Page: "vLLM-Omni 上的 MiniMax H3：从系统级优化到基于 FastVideo FastH
 (Chinese translation of the vLLM blog post), §4.3 and figure 6: Q, K, P and V are
 quantized to FP8 for both attention products.  The format (OCP E4M3 "fn": bias 7,
 3 mantissa bits, subnormals, largest finite 448) is pinned by brute force over its 254
-finite values; the quantizer by its extremes and error bound and by a case where the
-fp32 and fp64 decisions differ; the attention by closed forms (equal keys, one key,
-power-of-two scaling of a V channel) and by its distance from exact attention.
+finite values; the quantizer by its extremes and error bound and by exact rational
+arithmetic on values at and next to E4M3 rounding midpoints; the attention by closed
+forms (equal keys, one key, power-of-two scaling of a V channel, weights on either side
+of a midpoint, the factor 256, the streamed tiles, Skip-Softmax decisions) and by its
+distance from exact attention.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -31,10 +34,9 @@ def e4m3_table():
 
 TABLE = e4m3_table()
 
-# The P codes are decided in fp32 (the kernel's precision), including the running maxima
-# that form the carry factor between tiles, so closed forms involving a carry hold to fp32
-# rounding of those maxima (about 1e-7 relative), not to fp64.
-CARRY_RTOL = 1e-6
+# Every step is fp64, so closed forms involving exp() and a carry between tiles hold to
+# fp64 rounding.
+CARRY_RTOL = 1e-12
 VALUES = np.array(sorted({v for v, _ in TABLE}))
 CODE_OF = {}
 for v, c in TABLE:
@@ -109,30 +111,55 @@ def test_quantize_group_extremes_zero_and_error_bound():
     assert zs == 0.0 and np.all(z == 0)
 
 
-def test_quantize_decision_taken_in_fp32():
-    """Values x whose fp32 product x * (448/amax) lands exactly on an E4M3 midpoint
-    (a tie, resolved to the even code) while the exact product 448 x / amax lies to one
-    side of it: the oracle must follow the fp32 product, the kernel's precision."""
-    amax = np.float32(3.7)
-    inv32 = np.float32(448.0) / amax
+def nearest_e4m3_exact(t: Fraction) -> float:
+    """Brute force on an exact rational: the nearest finite E4M3 value, ties to the even
+    code, saturating at +-448."""
+    if t >= 448:
+        return 448.0
+    if t <= -448:
+        return -448.0
+    d = [abs(Fraction(float(v)) - t) for v in VALUES]
+    m = min(d)
+    best = [VALUES[i] for i, x in enumerate(d) if x == m]
+    if len(best) == 1:
+        return float(best[0])
+    return float([v for v in best if CODE_OF[v] % 2 == 0][0])
+
+
+def bf16_value(bits: int) -> float:
+    return float(np.array([bits << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+def test_quantize_decision_is_the_exact_one():
+    """The code of x in a group of maximum amax is the E4M3 rounding of the exact rational
+    448 x / amax.  Checked with Python fractions on bf16 pairs built to hit E4M3 midpoints
+    exactly (ties, which must go to the even code) and on their bf16 neighbours (one ulp
+    away, which must go to the nearer code), for amax with mantissas that make 448/amax
+    inexact in binary (3, 5, 7, 9, 11, 13 times a power of two) and exact (powers of
+    two)."""
     pos = VALUES[VALUES > 0]
-    found = 0
-    for a, b in zip(pos[:-1], pos[1:]):
-        t = (a + b) / 2
-        x0 = np.float32(t / float(inv32))
-        for step in range(-30, 31):
-            x = np.float32(x0)
-            for _ in range(abs(step)):
-                x = np.nextafter(x, np.float32(np.inf if step > 0 else -np.inf))
-            if not (0 < x < amax):
-                continue
-            y32 = float(np.float32(x) * inv32)
-            y_exact = float(x) * 448.0 / float(amax)
-            if y32 == t and nearest_e4m3(y_exact) != nearest_e4m3(y32):
-                codes, _ = O.quantize_group(np.array([amax, x], dtype=np.float32))
-                assert codes[1] == nearest_e4m3(y32), (x, y32, y_exact)
-                found += 1
-    assert found >= 3, found
+    mids = [(a + b) / 2 for a, b in zip(pos[:-1], pos[1:])]
+    ties = 0
+    checked = 0
+    for amax in (1.5, 2.5, 3.5, 4.5, 5.5, 6.5, 0.75, 4.0, 1.0, 0.3125, 6.0, 7.0, 112.0):
+        amax = bf16_value(O.round_bf16(amax))
+        for mid in mids:
+            x0 = mid * amax / 448.0
+            b0 = O.round_bf16(x0)
+            for bits in (b0 - 1, b0, b0 + 1):
+                x = bf16_value(bits)
+                if not (0 < x < amax):
+                    continue
+                t = Fraction(x) * 448 / Fraction(amax)
+                codes, scale = O.quantize_group(np.array([amax, x], dtype=np.float32))
+                assert codes[0] == 448.0 and scale == amax / 448.0
+                assert codes[1] == nearest_e4m3_exact(t), (amax, x, t)
+                checked += 1
+                if any(t == Fraction(float(m)) for m in mids):
+                    ties += 1
+                codes, _ = O.quantize_group(np.array([-amax, -x], dtype=np.float32))
+                assert codes[1] == -nearest_e4m3_exact(t)
+    assert ties >= 20 and checked > 400, (ties, checked)
 
 
 def bf16(x):
@@ -341,37 +368,10 @@ def test_skip_decides_against_the_running_maximum_before_the_tile():
                        rtol=CARRY_RTOL, atol=0)
 
 
-def test_allowance_zero_without_near_midpoint_weights_and_bounded_otherwise():
-    """The allowance covers P codes whose argument lies within the matrix cores' score
-    error of an E4M3 rounding midpoint.  In the two-key closed form (weights 256 and
-    E4M3(94.2) = 96, 2 % from the 88/96 midpoint 92, far beyond the 0.4 % window) it is
-    exactly 0; on random inputs it is finite, non-negative and small against the output."""
-    S, N, H, D = 2, 2, 1, 128
-    scale = 0.088
-    q = np.zeros((S, H, D))
-    q[:, 0, 0] = 2.0 / scale
-    k = np.zeros((S, H, D))
-    k[0, 0, 0], k[1, 0, 0] = 1.0, 0.5
-    v = np.zeros((S, H, D))
-    v[0] = 1.0
-    out, allow = O.attn_varlen_fp8(bf16(q), bf16(k), bf16(v), N, scale, np.array([0, 1]),
-                                   with_allowance=True)
-    assert np.all(allow == 0.0)
-    assert np.array_equal(out, O.attn_varlen_fp8(bf16(q), bf16(k), bf16(v), N, scale,
-                                                 np.array([0, 1])))
-    rng = np.random.default_rng(14)
-    S, N, H = 300, 290, 2
-    q, k, v = (bf16(rng.standard_normal((S, H, D))) for _ in range(3))
-    out, allow = O.attn_varlen_fp8(q, k, v, N, 1 / math.sqrt(D), np.arange(N),
-                                   with_allowance=True)
-    assert np.all(np.isfinite(allow)) and np.all(allow >= 0.0)
-    assert allow.mean() < 0.05 * np.abs(out).mean() + 1e-3
-
-
 def _two_key_case(alpha, **kw):
     """Query alpha * e_0 against keys e_0 and 0 (one 16-key block, amax 1), V rows 0 and
-    e_5.  In log2 units the key-0 score exceeds the key-1 score (0) by
-    alpha * fl(scale * log2 e), exactly as the codes are 448 and 0."""
+    e_5.  The key-0 score exceeds the key-1 score (0) by alpha * scale exactly (the codes
+    are 448 and 0, the scales alpha/448 and 1/448)."""
     D = 128
     q = np.zeros((2, 1, D))
     q[:, 0, 0] = alpha
@@ -380,7 +380,7 @@ def _two_key_case(alpha, **kw):
     v = np.zeros((2, 1, D))
     v[1, 0, 5] = 1.0
     return O.attn_varlen_fp8(bf16(q), bf16(k), bf16(v), 2, 1 / math.sqrt(D), np.array([0]),
-                             with_allowance=True, **kw)
+                             **kw)
 
 
 def test_p_is_256_times_the_weight_down_to_the_smallest_subnormal():
@@ -389,39 +389,32 @@ def test_p_is_256_times_the_weight_down_to_the_smallest_subnormal():
     o_5 = 2^-9 / (256 + 2^-9).  Any other power-of-two factor in
     front of the weights moves this key across the subnormal rounding point (at 128 it
     rounds to 0), so only the factor 256 gives this output."""
-    out, _ = _two_key_case(137.0)
+    out = _two_key_case(137.0)
     want = np.zeros(128)
     want[5] = 2.0 ** -9 / (256 + 2.0 ** -9)
     assert np.allclose(out[0, 0], want, rtol=1e-12, atol=0)
 
 
-def test_allowance_of_a_code_at_an_e4m3_midpoint():
-    """Key 1's weight 2^(8 - 1.4744) = 92.13 lies 0.14 % above the 88/96 midpoint 92, inside
-    the score-error window of the maximum (2^-9 of its 1.47 log2 units): the code is 96
-    (o_5 = 96 / 352), and the allowance is one step of 8 carried to the output,
-    8 * |v_1 - o| / (256 + 88) with the smaller of the two normalisers."""
-    out, allow = _two_key_case(11.5625)
-    o5 = 96.0 / (256 + 96)
-    assert abs(out[0, 0, 5] - o5) <= 1e-15
-    assert abs(allow[0, 0, 5] - 8 * (1 - o5) / (256 + 88)) <= 1e-12
-    assert np.all(allow[0, 0, np.arange(128) != 5] == 0.0)  # V is 0 there, as is o
+def test_weights_on_either_side_of_an_e4m3_midpoint():
+    """Key 1's weight is 256 exp(-alpha / sqrt(128)).  alpha = 11.5625 gives 92.13, 0.14 %
+    above the 88/96 midpoint 92, so the code is 96 and o_5 = 96 / 352; alpha = 11.6250
+    gives 91.51, below it, so the code is 88 and o_5 = 88 / 344.  The two alphas are
+    bf16 values, so the scores are exact."""
+    for alpha, code in ((11.5625, 96.0), (11.625, 88.0)):
+        w = 256.0 * math.exp(-alpha / math.sqrt(128))
+        assert (w > 92.0) == (code == 96.0) and abs(w - 92.0) < 1.0
+        out = _two_key_case(alpha)
+        want = np.zeros(128)
+        want[5] = code / (256.0 + code)
+        assert np.allclose(out[0, 0], want, rtol=1e-14, atol=0), (alpha, out[0, 0, 5])
 
 
-def test_allowance_of_a_skip_decision_at_its_threshold():
-    """One key per tile; key 1 sits g = 1.4744 log2 units below the maximum, its code 96.
-    A threshold 2^(-g + 0.001) lies inside the window (2^-9 of the maximum's 1.47 units)
-    and drops the tile: o_5 = 0, and the allowance is the tile's 96 against the smallest
-    normaliser the flip could leave, 96 / (256 - 96).  At 2^(-g - 0.001) the tile is kept
-    (o_5 = 96/352) with allowance 96 * (1 - 96/352) / 256; at 2^(-g + 0.01), outside the
-    window, the drop is certain and the allowance 0."""
-    g = float(np.float32(11.5625) * np.float32(np.float32(1 / math.sqrt(128)) *
-                                              np.float32(1.4426950408889634)))
-    out, allow = _two_key_case(11.5625, p_tile=1, skip_threshold=2.0 ** (-g + 0.001))
+def test_skip_decision_at_a_fine_margin_from_its_threshold():
+    """One key per tile; key 1 sits g = alpha / sqrt(128) nats below the maximum.  A
+    threshold exp(-g + 1e-9) drops the tile (o_5 = 0), exp(-g - 1e-9) keeps it
+    (o_5 = 96 / 352): the decision is taken on the exact scores, down to fp64 rounding."""
+    g = 11.5625 / math.sqrt(128)
+    out = _two_key_case(11.5625, p_tile=1, skip_threshold=math.exp(-g + 1e-9))
     assert out[0, 0, 5] == 0.0
-    assert abs(allow[0, 0, 5] - 96.0 / (256 - 96)) <= 1e-12
-    out, allow = _two_key_case(11.5625, p_tile=1, skip_threshold=2.0 ** (-g - 0.001))
-    o5 = 96.0 / 352
-    assert abs(out[0, 0, 5] - o5) <= 1e-15
-    assert abs(allow[0, 0, 5] - 96 * (1 - o5) / 256) <= 1e-12
-    out, allow = _two_key_case(11.5625, p_tile=1, skip_threshold=2.0 ** (-g + 0.01))
-    assert out[0, 0, 5] == 0.0 and np.all(allow == 0.0)
+    out = _two_key_case(11.5625, p_tile=1, skip_threshold=math.exp(-g - 1e-9))
+    assert abs(out[0, 0, 5] - 96.0 / 352) <= 1e-15
