@@ -9,7 +9,9 @@ inputs already resident in HBM.  Prints one JSON line:
   roofline   the dominant kernel (attention, timed alone via h3_attn_packed with HIP
              events on the launch stream) against the bf16 dense MFMA peak
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload
-             (sampled query rows of every head), whose rows also gate parity
+             (sampled query rows of every head), whose rows also gate parity: the check
+             runs on the first h3_attn_layer call, before anything is timed, and a run
+             that fails it prints a line with no `value` and exits non-zero
   kernels    the other kernels' achieved bandwidth (K/V pre-pass, standalone prologue, the
              fused residual + LayerNorm + modulation steps around attention)
   fp8        the FP8 (SAGE) variant on the same workload: h3_attn_layer_fp8 per step, its
@@ -21,9 +23,10 @@ inputs already resident in HBM.  Prints one JSON line:
   per_workload  every workload size: h3_attn_layer and h3_attn_varlen TFLOP/s (median and
              min of 10 calls after 3 warm-up calls), the same for the FP8 calls,
              h3_qk_rmsnorm_rope GB/s, and (unless --no-cpu-baseline) `oracle`: the fp64
-             oracle timed on every row of the short workloads and on sampled rows of the
-             long ones (with the full-layer time extrapolated), checked against the
-             layer's output on those rows
+             oracle timed on every row of the short workloads and on 4,096 sampled rows
+             per head of the long ones (with the full-layer time extrapolated), checked
+             against the layer's output on those rows before the workload is timed (a
+             workload that fails is not timed)
   sclk_mhz   the shader clock the driver reported right after the timed region
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
@@ -150,13 +153,15 @@ def oracle_check(W, w, inp, out_rows, rows, scale):
             "ok": ok}
 
 
-def per_workload(torch, B, W, dev, stream, oracle_rows=None):
+def per_workload(torch, B, W, dev, stream, oracle_rows=None, known=None):
     """h3_attn_layer / h3_attn_varlen TFLOP/s and prologue GB/s on every workload size;
-    with `oracle_rows`, also the fp64 oracle timed on that many sampled rows per head
+    with `oracle_rows`, first the fp64 oracle timed on that many sampled rows per head
     (every row of the workloads with at most 8,192 valid tokens) and checked against the
-    layer's output."""
+    layer's output; a workload that fails the check is not timed.  `known`: {index:
+    check} already made on the same inputs (the headline workload's)."""
     import statistics
     table = {}
+    known = known or {}
     for idx, w in sorted(W.WORKLOADS.items()):
         inp = W.generate(w, tail="nan")
         d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
@@ -165,8 +170,8 @@ def per_workload(torch, B, W, dev, stream, oracle_rows=None):
         n = d["n_valid"]
         out = torch.empty_like(d["q"])
         ws = torch.empty(B.workspace_size(d["q"]), dtype=torch.uint8, device=dev)
-        orc = None
-        if oracle_rows is not None:
+        orc = known.get(idx)
+        if orc is None and oracle_rows is not None:
             rows = (list(range(w.n_valid)) if w.n_valid <= 8192
                     else W.sample_rows(w, oracle_rows, 40_000 + idx))
             B.attn_layer(d["q"], d["k"], d["v"], d["w_q"], d["w_k"], n, w.eps, rope, scale,
@@ -174,10 +179,18 @@ def per_workload(torch, B, W, dev, stream, oracle_rows=None):
             idx_t = torch.as_tensor(rows, dtype=torch.long, device=dev)
             got = out[0].index_select(0, idx_t).double().cpu().numpy()
             orc = oracle_check(W, w, inp, got, rows, scale)
-            log(f"[bench] {w.name}: oracle {orc['seconds']}s on {len(rows)} rows/head, "
-                f"max {orc['max_abs']:.2e} mean {orc['mean_abs']:.2e} relL2 "
+        if orc is not None:
+            log(f"[bench] {w.name}: oracle {orc['seconds']}s on {orc['rows_per_head']} "
+                f"rows/head, max {orc['max_abs']:.2e} mean {orc['mean_abs']:.2e} relL2 "
                 f"{orc['rel_l2']:.2e} -> {'ok' if orc['ok'] else 'FAIL'}")
         del inp
+        if orc is not None and not orc["ok"]:
+            table[w.name] = {"heads": w.heads, "n_valid": w.n_valid, "seq_buf": w.seq_buf,
+                             "oracle": orc, "timed": False}
+            log(f"[bench] {w.name}: parity FAILED, not timed")
+            del d, out, ws
+            torch.cuda.empty_cache()
+            continue
         ws8 = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
         q2, k2 = torch.empty_like(d["q"]), torch.empty_like(d["k"])
         row = {"heads": w.heads, "n_valid": w.n_valid, "seq_buf": w.seq_buf,
@@ -230,6 +243,21 @@ def copy_only(torch, dev, steps: int) -> int:
     return 0
 
 
+def workload_config(w) -> dict:
+    return {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim,
+            "n_valid": w.n_valid, "seq_buf": w.seq_buf, "batch": w.batch,
+            "entry": "h3_attn_layer", "rope": "1-D" if w.n_1d is None else "1-D+3-axis",
+            "parallelism": "single GPU"}
+
+
+def refusal(w, check: dict) -> str:
+    """The one JSON line of a run whose parity check failed: nothing was timed, so there
+    is no `value`."""
+    return json.dumps({"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "data": "synthetic",
+                       "config": workload_config(w), "parity": check,
+                       "error": "h3_attn_layer does not match the fp64 oracle; not timed"})
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,7 +265,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-rows-per-head", type=int, default=4096)
-    ap.add_argument("--oracle-rows-per-head", type=int, default=256,
+    ap.add_argument("--oracle-rows-per-head", type=int, default=4096,
                     help="sampled rows per head of the per-workload oracle check on the "
                          "long workloads (the short ones are checked on every row)")
     ap.add_argument("--no-per-workload", action="store_true")
@@ -300,6 +328,25 @@ def main() -> int:
             log(f"[bench] fp8 attention launch {i + 1}/{args.steps} done")
         return 0
 
+    # ---- parity first: the first h3_attn_layer call against the fp64 oracle on sampled
+    # rows of every head (the CPU baseline's sample; 64 rows per head with
+    # --no-cpu-baseline).  A failing configuration is not timed.
+    step()
+    torch.cuda.synchronize()
+    layer_out = out.clone()
+    rows = W.sample_rows(w, 64 if args.no_cpu_baseline else args.cpu_rows_per_head,
+                         30_000 + args.workload)
+    idx = torch.as_tensor(rows, dtype=torch.long, device=dev)
+    got = layer_out[0].index_select(0, idx).double().cpu().numpy()
+    log(f"[bench] oracle on {len(rows)} rows x {w.heads} heads before timing")
+    check = oracle_check(W, w, inp, got, rows, scale)
+    log(f"[bench] oracle {check['seconds']}s; parity max {check['max_abs']:.2e} mean "
+        f"{check['mean_abs']:.2e} relL2 {check['rel_l2']:.2e} -> "
+        f"{'ok' if check['ok'] else 'FAIL'}")
+    if not check["ok"]:
+        print(refusal(w, check), flush=True)
+        return 1
+
     # ---- headline: K whole-layer steps
     for _ in range(args.warmup):
         step()
@@ -319,7 +366,8 @@ def main() -> int:
     value = flops / (ms_step * 1e-3) / 1e12
     log(f"[bench] h3_attn_layer {ms_step:.3f} ms/step  {value:.1f} TFLOP/s "
         f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of bf16 peak), wall {wall:.3f}s")
-    layer_out = out.clone()
+    assert torch.equal(out.view(torch.int16), layer_out.view(torch.int16)), \
+        "timed calls differ from the checked call"
 
     # ---- dominant kernel alone: attention from packed K/V (fused Q prologue).  One call
     # is the fast pass plus the checked pass, which returns at once for workgroups the
@@ -483,10 +531,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "heads": w.heads, "head_dim": w.head_dim,
-                   "n_valid": w.n_valid, "seq_buf": w.seq_buf, "batch": w.batch,
-                   "entry": "h3_attn_layer", "rope": "1-D" if w.n_1d is None else "1-D+3-axis",
-                   "parallelism": "single GPU"},
+        "config": workload_config(w),
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -518,49 +563,30 @@ def main() -> int:
         "source_hash": source_hash(),
     }
 
-    # ---- CPU baseline: the fp64 oracle on sampled rows of every head
+    # ---- CPU baseline: the fp64 oracle's time on the sample checked before timing
+    result["parity"] = {k: check[k] for k in ("rows_per_head", "max_abs", "mean_abs",
+                                               "rel_l2", "ok")}
     if not args.no_cpu_baseline:
         from oracle import oracle as O
-        rows = W.sample_rows(w, args.cpu_rows_per_head, 30_000 + args.workload)
-        threads = O.default_threads()
-        orope = O.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
-        log(f"[bench] oracle on {len(rows)} rows x {w.heads} heads, {threads} threads")
-        t0 = time.perf_counter()
-        ref = O.attn_layer(W.bits(inp["q"][0]), W.bits(inp["k"][0]), W.bits(inp["v"][0]),
-                           w.n_valid, W.bits(inp["w_q"]), W.bits(inp["w_k"]), w.eps, orope,
-                           scale, np.asarray(rows, dtype=np.int64), threads=threads)
-        t_cpu = time.perf_counter() - t0
-        cpu_flops = 4.0 * len(rows) * w.n_valid * w.head_dim * w.heads
-        idx = torch.as_tensor(rows, dtype=torch.long, device=dev)
-        got = layer_out[0].index_select(0, idx).float().cpu().numpy().astype(np.float64)
-        err = np.abs(got - ref)
-        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-        parity_ok = bool(err.max() <= 1.5e-2 and err.mean() <= 2e-3 and rel <= 1e-2)
-        log(f"[bench] oracle {t_cpu:.1f}s; parity max {err.max():.2e} mean {err.mean():.2e} "
-            f"relL2 {rel:.2e} -> {'ok' if parity_ok else 'FAIL'}")
+        cpu_tflops = check["tflops_fp64"]
         result["cpu_baseline"] = {
-            "value": round(cpu_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "value": cpu_tflops, "unit": "TFLOP/s", "cores": check["threads"],
             "kind": "oracle",
             "sample": f"{len(rows)} sampled query rows x {w.heads} heads of {w.name} "
-                      f"(all {w.n_valid} keys each), fp64, {t_cpu:.1f} s",
-            "seconds": round(t_cpu, 2),
-            "extrapolated_full_layer_s": round(t_cpu * w.n_valid / len(rows), 1),
+                      f"(all {w.n_valid} keys each), fp64, {check['seconds']} s",
+            "seconds": check["seconds"],
+            "extrapolated_full_layer_s": check["extrapolated_full_layer_s"],
             "cpu_model": cpu_model(),
             "affinity_cpus": len(os.sched_getaffinity(0)),
-            "gpu_over_cpu": round(value / (cpu_flops / t_cpu / 1e12), 1),
+            "gpu_over_cpu": round(value / cpu_tflops, 1),
         }
-        result["parity"] = {"rows": len(rows), "max_abs": float(err.max()),
-                            "mean_abs": float(err.mean()), "rel_l2": rel, "ok": parity_ok}
-        if not parity_ok:
-            print(json.dumps(result), flush=True)
-            log("[bench] parity FAILED against the oracle")
-            return 1
     if not args.no_per_workload:
         del d, out, ws, q2, k2, layer_out
         torch.cuda.empty_cache()
         result["per_workload"] = per_workload(
             torch, B, W, dev, stream,
-            None if args.no_cpu_baseline else args.oracle_rows_per_head)
+            None if args.no_cpu_baseline else args.oracle_rows_per_head,
+            known=None if args.no_cpu_baseline else {args.workload: check})
     print(json.dumps(result), flush=True)
     return 0
 

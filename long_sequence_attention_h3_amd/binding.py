@@ -116,12 +116,16 @@ def _check(status: int, what: str):
         raise H3Error(status, f"{what}: {msg}")
 
 
+def _on_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
 def _row_stride(t: torch.Tensor, name: str) -> int:
     """Row stride (elements) of a [B, S, H, D] or [S, H, D] bf16 device tensor whose heads
     and channels are packed and whose batches are S rows apart."""
     if t.dtype != torch.bfloat16:
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
-    if not t.is_cuda:
+    if not _on_device(t):
         raise ValueError(f"{name} must be a device tensor")
     if t.dim() == 3:
         t = t.unsqueeze(0)
@@ -137,6 +141,43 @@ def _row_stride(t: torch.Tensor, name: str) -> int:
 
 def _dims(t: torch.Tensor):
     return (1, *t.shape) if t.dim() == 3 else tuple(t.shape)
+
+
+def _like(t: torch.Tensor, ref: torch.Tensor, name: str, ref_name: str = "q") -> int:
+    """Row stride of ``t`` after checking that it is a bf16 tensor on ``ref``'s device with
+    ``ref``'s [B, S, H, D] shape (so no kernel can read or write past its end)."""
+    stride = _row_stride(t, name)
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, {ref_name} on {ref.device}")
+    if _dims(t) != _dims(ref):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, {ref_name} {tuple(ref.shape)}")
+    return stride
+
+
+def _weight_stride(x: torch.Tensor, *ws) -> int:
+    """w_head_stride for norm weights ``ws`` (all present, or all None -> 0): bf16 device
+    tensors on ``x``'s device, each [D] (shared by the heads) or [H, D] with packed
+    channels, all with the same shape and strides."""
+    if all(w is None for w in ws):
+        return 0
+    if any(w is None for w in ws):
+        raise ValueError("w_q and w_k must both be given")
+    _, _, H, D = _dims(x)
+    first = ws[0]
+    for w in ws:
+        if w.dtype != torch.bfloat16 or not _on_device(w) or w.device != x.device:
+            raise ValueError(f"norm weights must be bf16 tensors on {x.device}")
+        if w.shape != first.shape or w.stride() != first.stride():
+            raise ValueError("w_q and w_k must have the same shape and strides")
+    if first.dim() == 1:
+        if first.shape != (D,) or first.stride(0) != 1:
+            raise ValueError(f"shared norm weights must be a contiguous [{D}] tensor")
+        return 0
+    if first.dim() != 2 or first.shape != (H, D) or first.stride(1) != 1:
+        raise ValueError(f"per-head norm weights must be [{H}, {D}] with packed channels")
+    if first.stride(0) < D or first.stride(0) % 8:
+        raise ValueError("per-head norm weights: head stride must be >= D and a multiple of 8")
+    return first.stride(0)
 
 
 class _Call:
@@ -157,6 +198,10 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def _p(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -174,8 +219,12 @@ def _workspace(q: torch.Tensor, call: _Call, workspace, fp8: bool = False):
     need = int(f(ctypes.byref(call.shape)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if workspace.numel() < need:
-        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    if not _on_device(workspace) or workspace.device != q.device or \
+            not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous device tensor on {q.device}")
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} "
+                         f"bytes, {need} needed")
     return workspace
 
 
@@ -184,15 +233,16 @@ def qk_rmsnorm_rope(q, k, w_q, w_k, n_valid, eps: float, rope: Rope, q_out=None,
     """Fused per-head Q/K RMSNorm + RoPE (h3_qk_rmsnorm_rope).  Returns (q_out, k_out);
     pass ``q_out=q, k_out=k`` to work in place.  Output rows [N, S) are not written."""
     s_in = _row_stride(q, "q")
-    if _row_stride(k, "k") != s_in:
+    if _like(k, q, "k") != s_in:
         raise ValueError("q and k must share a row stride")
     q_out = torch.empty_like(q) if q_out is None else q_out
     k_out = torch.empty_like(k) if k_out is None else k_out
-    s_out = _row_stride(q_out, "q_out")
-    if _row_stride(k_out, "k_out") != s_out:
+    s_out = _like(q_out, q, "q_out")
+    if _like(k_out, q, "k_out") != s_out:
         raise ValueError("q_out and k_out must share a row stride")
-    H = q.shape[-2]
-    w_head_stride = 0 if w_q.dim() == 1 else w_q.stride(0)
+    w_head_stride = _weight_stride(q, w_q, w_k)
+    if w_q is None:
+        raise ValueError("w_q and w_k are required")
     call = _Call(q, n_valid, s_in, s_out)
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_qk_rmsnorm_rope(_p(q), _p(k), _p(q_out), _p(k_out), _p(w_q), _p(w_k),
@@ -206,17 +256,12 @@ def attn_varlen(q, k, v, n_valid, softmax_scale: float, out=None, workspace=None
                 stream=None):
     """Attention over the valid tokens with pre-normalised, pre-rotated Q/K
     (h3_attn_varlen).  Output rows [N, S) are zero."""
-    s_in = _row_stride(q, "q")
-    for name, t in (("k", k), ("v", v)):
-        if _row_stride(t, name) != s_in:
-            raise ValueError("q, k and v must share a row stride")
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
-    s_out = _row_stride(out, "out")
+    s_in, out, s_out = _qkv_strides(q, k, v, out)
     call = _Call(q, n_valid, s_in, s_out)
     ws = _workspace(q, call, workspace)
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_varlen(_p(q), _p(k), _p(v), _p(out), float(softmax_scale),
-                                ctypes.byref(call.shape), _p(ws), ws.numel(),
+                                ctypes.byref(call.shape), _p(ws), _nbytes(ws),
                                 ctypes.c_void_p(st)), "h3_attn_varlen")
     return out
 
@@ -224,19 +269,16 @@ def attn_varlen(q, k, v, n_valid, softmax_scale: float, out=None, workspace=None
 def attn_layer(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_scale: float,
                out=None, workspace=None, stream=None):
     """The whole layer: Q/K RMSNorm + RoPE fused into attention (h3_attn_layer)."""
-    s_in = _row_stride(q, "q")
-    for name, t in (("k", k), ("v", v)):
-        if _row_stride(t, name) != s_in:
-            raise ValueError("q, k and v must share a row stride")
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
-    s_out = _row_stride(out, "out")
-    w_head_stride = 0 if w_q.dim() == 1 else w_q.stride(0)
+    s_in, out, s_out = _qkv_strides(q, k, v, out)
+    if w_q is None or w_k is None:
+        raise ValueError("w_q and w_k are required")
+    w_head_stride = _weight_stride(q, w_q, w_k)
     call = _Call(q, n_valid, s_in, s_out)
     ws = _workspace(q, call, workspace)
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_layer(_p(q), _p(k), _p(v), _p(out), _p(w_q), _p(w_k), w_head_stride,
                                float(eps), ctypes.byref(rope), float(softmax_scale),
-                               ctypes.byref(call.shape), _p(ws), ws.numel(),
+                               ctypes.byref(call.shape), _p(ws), _nbytes(ws),
                                ctypes.c_void_p(st)), "h3_attn_layer")
     return out
 
@@ -247,15 +289,15 @@ def kv_pack(k, v, n_valid, workspace=None, w_k=None, eps: float = 0.0, rope: Rop
     ``softmax_scale * log2(e)`` before rounding, when ``w_k`` is given) and V into a
     workspace for h3_attn_packed.  Returns the workspace."""
     s_in = _row_stride(k, "k")
-    if _row_stride(v, "v") != s_in:
+    if _like(v, k, "v", "k") != s_in:
         raise ValueError("k and v must share a row stride")
+    w_head_stride = _weight_stride(k, w_k)
     call = _Call(k, n_valid, s_in, s_in)
     ws = _workspace(k, call, workspace)
-    w_head_stride = 0 if (w_k is None or w_k.dim() == 1) else w_k.stride(0)
     st = _stream(k.device) if stream is None else stream
     _check(lib().h3_kv_pack(_p(k), _p(v), _p(w_k), w_head_stride, float(eps),
                             ctypes.byref(rope) if rope is not None else None,
-                            float(softmax_scale), ctypes.byref(call.shape), _p(ws), ws.numel(),
+                            float(softmax_scale), ctypes.byref(call.shape), _p(ws), _nbytes(ws),
                             ctypes.c_void_p(st)),
            "h3_kv_pack")
     return ws
@@ -267,24 +309,34 @@ def attn_packed(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: floa
     ``w_q`` is given) against K/V packed by ``kv_pack``."""
     s_in = _row_stride(q, "q")
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
-    s_out = _row_stride(out, "out")
+    s_out = _like(out, q, "out")
+    w_head_stride = _weight_stride(q, w_q)
     call = _Call(q, n_valid, s_in, s_out)
-    w_head_stride = 0 if (w_q is None or w_q.dim() == 1) else w_q.stride(0)
+    _check_packed(q, call, workspace, fp8=False)
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_packed(_p(q), _p(out), _p(w_q), w_head_stride, float(eps),
                                 ctypes.byref(rope) if rope is not None else None,
                                 float(softmax_scale), ctypes.byref(call.shape), _p(workspace),
-                                workspace.numel(), ctypes.c_void_p(st)), "h3_attn_packed")
+                                _nbytes(workspace), ctypes.c_void_p(st)), "h3_attn_packed")
     return out
 
 
 def _qkv_strides(q, k, v, out):
+    """Row strides of q (shared by k and v) and out, after checking that k, v and out
+    are bf16 tensors on q's device with q's shape; allocates out when it is None."""
     s_in = _row_stride(q, "q")
     for name, t in (("k", k), ("v", v)):
-        if _row_stride(t, name) != s_in:
+        if _like(t, q, name) != s_in:
             raise ValueError("q, k and v must share a row stride")
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
-    return s_in, out, _row_stride(out, "out")
+    return s_in, out, _like(out, q, "out")
+
+
+def _check_packed(q, call: _Call, workspace, fp8: bool):
+    """A packed-stage workspace must be a device tensor on q's device."""
+    if not isinstance(workspace, torch.Tensor) or not _on_device(workspace) or \
+            workspace.device != q.device:
+        raise ValueError(f"workspace must be a device tensor on {q.device}")
 
 
 def attn_varlen_fp8(q, k, v, n_valid, softmax_scale: float, out=None, workspace=None,
@@ -297,7 +349,7 @@ def attn_varlen_fp8(q, k, v, n_valid, softmax_scale: float, out=None, workspace=
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_varlen_fp8(_p(q), _p(k), _p(v), _p(out), float(softmax_scale),
                                     float(skip_threshold), ctypes.byref(call.shape), _p(ws),
-                                    ws.numel(),
+                                    _nbytes(ws),
                                     ctypes.c_void_p(st)), "h3_attn_varlen_fp8")
     return out
 
@@ -306,14 +358,16 @@ def attn_layer_fp8(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_s
                    out=None, workspace=None, stream=None, skip_threshold: float = 0.0):
     """The whole layer with FP8 attention: Q/K RMSNorm + RoPE fused (h3_attn_layer_fp8)."""
     s_in, out, s_out = _qkv_strides(q, k, v, out)
-    w_head_stride = 0 if w_q.dim() == 1 else w_q.stride(0)
+    if w_q is None or w_k is None:
+        raise ValueError("w_q and w_k are required")
+    w_head_stride = _weight_stride(q, w_q, w_k)
     call = _Call(q, n_valid, s_in, s_out)
     ws = _workspace(q, call, workspace, fp8=True)
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_layer_fp8(_p(q), _p(k), _p(v), _p(out), _p(w_q), _p(w_k),
                                    w_head_stride, float(eps), ctypes.byref(rope),
                                    float(softmax_scale), float(skip_threshold),
-                                   ctypes.byref(call.shape), _p(ws), ws.numel(),
+                                   ctypes.byref(call.shape), _p(ws), _nbytes(ws),
                                    ctypes.c_void_p(st)), "h3_attn_layer_fp8")
     return out
 
@@ -323,15 +377,15 @@ def kv_pack_fp8(k, v, n_valid, workspace=None, w_k=None, eps: float = 0.0,
     """FP8 stage 1 (h3_kv_pack_fp8): quantize K (normalised + rotated when ``w_k`` is
     given) and V into FP8 tiles for h3_attn_packed_fp8.  Returns the workspace."""
     s_in = _row_stride(k, "k")
-    if _row_stride(v, "v") != s_in:
+    if _like(v, k, "v", "k") != s_in:
         raise ValueError("k and v must share a row stride")
+    w_head_stride = _weight_stride(k, w_k)
     call = _Call(k, n_valid, s_in, s_in)
     ws = _workspace(k, call, workspace, fp8=True)
-    w_head_stride = 0 if (w_k is None or w_k.dim() == 1) else w_k.stride(0)
     st = _stream(k.device) if stream is None else stream
     _check(lib().h3_kv_pack_fp8(_p(k), _p(v), _p(w_k), w_head_stride, float(eps),
                                 ctypes.byref(rope) if rope is not None else None,
-                                ctypes.byref(call.shape), _p(ws), ws.numel(),
+                                ctypes.byref(call.shape), _p(ws), _nbytes(ws),
                                 ctypes.c_void_p(st)), "h3_kv_pack_fp8")
     return ws
 
@@ -343,14 +397,15 @@ def attn_packed_fp8(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: 
     registers when ``w_q`` is given) against FP8 tiles packed by ``kv_pack_fp8``."""
     s_in = _row_stride(q, "q")
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
-    s_out = _row_stride(out, "out")
+    s_out = _like(out, q, "out")
+    w_head_stride = _weight_stride(q, w_q)
     call = _Call(q, n_valid, s_in, s_out)
-    w_head_stride = 0 if (w_q is None or w_q.dim() == 1) else w_q.stride(0)
+    _check_packed(q, call, workspace, fp8=True)
     st = _stream(q.device) if stream is None else stream
     _check(lib().h3_attn_packed_fp8(_p(q), _p(out), _p(w_q), w_head_stride, float(eps),
                                     ctypes.byref(rope) if rope is not None else None,
                                     float(softmax_scale), float(skip_threshold),
-                                    ctypes.byref(call.shape), _p(workspace), workspace.numel(),
+                                    ctypes.byref(call.shape), _p(workspace), _nbytes(workspace),
                                     ctypes.c_void_p(st)), "h3_attn_packed_fp8")
     return out
 

@@ -9,8 +9,9 @@ import torch
 from long_sequence_attention_h3_amd import binding as B
 from long_sequence_attention_h3_amd import workloads as W
 
-from parity_helpers import (assert_close, assert_tail_zero, gpu_layer, gpu_rope, gpu_varlen,
-                            oracle_layer, oracle_varlen, rows_of, say, scale_of, to_dev)
+from parity_helpers import (MAX_ABS, MEAN_ABS, REL_L2, assert_close, assert_tail_zero, errors,
+                            gpu_layer, gpu_rope, gpu_varlen, oracle_layer, oracle_varlen,
+                            rows_of, say, scale_of, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -148,12 +149,12 @@ def test_large_scores_mix_both_passes(dev):
     """Scores far above tile 0's row maximum.  Query rows [256, 512) scaled by 8 (their
     256-row workgroup must take the checked pass, the others the fast one) and key 1400
     scaled by 3 (the fast pass then runs with a running max below the true maximum);
-    every row against the oracle.  The layer variant scales head 1's w_q by 8: logits
-    that large magnify the unavoidable bf16 rounding of the normalised Q and K that the
-    matrix cores consume (about 2^-9 relative per element), so that variant is checked
-    against the oracle's fp64 prologue rounded as the layer rounds it (Q to bf16; K times
-    c = softmax_scale * log2(e) in fp32, then to bf16), then the oracle's attention with
-    the scale divided by c."""
+    every row against the oracle.  The layer variant scales head 1's w_q by 8, so its
+    logits are 8x the workload's, and compares with the plain fp64 oracle: head 0 at the
+    layer's bar, head 1 at that bar with its absolute terms scaled by the logit factor
+    (the products consume the normalised Q and K rounded to bf16, 2^-9 relative per
+    element as in any bf16 attention, so the score errors and, to first order, the
+    output errors grow with the logits; relative L2 keeps its 1e-2 gate)."""
     from oracle import oracle as O
     n, s = 1500, 1536
     w = small(n, s, heads=2, seed=57)
@@ -174,27 +175,25 @@ def test_large_scores_mix_both_passes(dev):
     rows = list(range(n))
     assert_close(rows_of(out, rows), oracle_varlen(w, inp, rows), "large scores varlen")
 
+    factor = 8.0
     wq = torch.stack([inp["w_q"], inp["w_q"]]).float()
-    wq[1] *= 8
+    wq[1] *= factor
     wq = wq.to(torch.bfloat16)
     wk = torch.stack([inp["w_k"], inp["w_k"]])
     say("[edge] large scores, layer (head 1 w_q x 8)")
     out = B.attn_layer(d["q"], d["k"], d["v"], wq.to(dev), wk.to(dev), n, w.eps, gpu_rope(w),
                        scale_of(w))
     torch.cuda.synchronize()
-    rope = O.make_rope(w.theta, w.rope_n_1d, w.sections, w.grid)
-
-    def normed_bf16(x, wt, mul=1.0):  # [S, H, D] bf16: oracle prologue times mul, rounded
-        y = O.prologue(W.bits(x), n, W.bits(wt), w.eps, rope, np.arange(n), w_head_stride=128)
-        full = torch.zeros((s, 2, 128), dtype=torch.bfloat16)
-        full[:n] = (torch.from_numpy(y).to(torch.float32) * mul).to(torch.bfloat16)
-        return full
-
-    c = float(np.float32(scale_of(w)) * np.float32(1.4426950408889634))
-    ref = O.attn_varlen(W.bits(normed_bf16(inp["q"][0], wq)),
-                        W.bits(normed_bf16(inp["k"][0], wk, c)), W.bits(inp["v"][0]), n,
-                        scale_of(w) / c, np.asarray(rows))
-    assert_close(rows_of(out, rows), ref, "large scores layer")
+    ref = O.attn_layer(W.bits(inp["q"][0]), W.bits(inp["k"][0]), W.bits(inp["v"][0]), n,
+                       W.bits(wq), W.bits(wk), w.eps, O.make_rope(w.theta, n), scale_of(w),
+                       np.asarray(rows), w_head_stride=128)
+    got = rows_of(out, rows)
+    assert_close(got[:, 0], ref[:, 0], "large scores layer, head 0")
+    assert np.all(np.isfinite(got[:, 1]))
+    mx, mean, rel = errors(got[:, 1], ref[:, 1])
+    say(f"  large scores layer, head 1 (logits x8): max|d|={mx:.3e} mean|d|={mean:.3e} "
+        f"relL2={rel:.3e}")
+    assert mx <= factor * MAX_ABS and mean <= factor * MEAN_ABS and rel <= REL_L2
 
 
 def test_equal_keys_give_mean_of_values_at_full_length(dev):

@@ -68,3 +68,27 @@ def test_bench_oracle_check_gates_parity():
     assert not good["all_rows"] and good["extrapolated_full_layer_s"] >= good["seconds"]
     bad = bench.oracle_check(W, w, inp, np.zeros_like(ref), rows, scale)
     assert not bad["ok"]
+
+
+def test_bench_refuses_to_report_a_value_when_parity_fails():
+    """A failing parity check yields a JSON line with no `value` (and main returns 1
+    before any timing); the check comes before the first timed event in main."""
+    from long_sequence_attention_h3_amd import workloads as W
+    w = W.WORKLOADS[3]
+    bad = {"rows_per_head": 4096, "max_abs": 0.03, "mean_abs": 0.005, "rel_l2": 0.5,
+           "ok": False}
+    line = json.loads(bench.refusal(w, bad))
+    assert "value" not in line and line["parity"]["ok"] is False
+    assert line["config"]["workload"] == w.name and line["metric"] == bench.METRIC
+    import inspect
+    src = inspect.getsource(bench.main)
+    check_at = src.index("check = oracle_check(")
+    refuse_at = src.index("print(refusal(w, check)")
+    assert check_at < refuse_at < src.index("e0.record(stream)")
+    assert "return 1" in src[refuse_at:refuse_at + 80]
+
+
+def test_per_workload_skips_timing_of_a_failed_workload():
+    import inspect
+    src = inspect.getsource(bench.per_workload)
+    assert src.index('if orc is not None and not orc["ok"]:') < src.index("call_times(")
