@@ -55,7 +55,9 @@ typedef enum {
   H3_ERR_UNSUPPORTED = 4,  /* head_dim != 128, bad RoPE sections or grid            */
   H3_ERR_DEVICE = 5,       /* no current HIP device, or it is not gfx950            */
   H3_ERR_LAUNCH = 6,       /* a kernel launch failed                                */
-  H3_ERR_WORKSPACE = 7     /* workspace missing or smaller than h3_attn_workspace_size */
+  H3_ERR_WORKSPACE = 7,    /* workspace missing or smaller than h3_attn_workspace_size */
+  H3_ERR_SCRATCH_LIMIT = 8 /* h3_attn_layer_noalloc: the problem needs more workspace than
+                              h3_attn_layer_noalloc_max_workspace() bytes            */
 } h3_status;
 
 /* One packed, aligned buffer ([Blog §3.1]: a valid length inside an aligned buffer). */
@@ -175,6 +177,26 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
                         const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
                         const h3_rope* rope, float softmax_scale, const h3_shape* shape,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The same layer for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): h3_attn_layer with its
+ * workspace in a static 64 MiB device array inside the library instead of a caller
+ * buffer.  It calls no hipMalloc, hipFree or allocating library routine; each GPU the
+ * library runs on holds its own copy of the array from first use until the process
+ * ends.  The caller still passes every input and output.  Output and errors as
+ * h3_attn_layer (bit-identical results), plus H3_ERR_SCRATCH_LIMIT, returned before any
+ * launch, when h3_attn_workspace_size(shape) exceeds
+ * h3_attn_layer_noalloc_max_workspace() (e.g. 8 heads x 8,192 tokens fit, 6 heads x
+ * 58,816 do not).  Every call on one GPU shares that GPU's array, so calls that overlap
+ * on one GPU (concurrent streams or threads) race; serialise them. */
+h3_status h3_attn_layer_noalloc(const void* q, const void* k, const void* v, void* o,
+                                const void* w_q, const void* w_k, int64_t w_head_stride,
+                                float eps, const h3_rope* rope, float softmax_scale,
+                                const h3_shape* shape, hipStream_t stream);
+
+/* Bytes of the static scratch behind h3_attn_layer_noalloc (the largest
+ * h3_attn_workspace_size it accepts). */
+size_t h3_attn_layer_noalloc_max_workspace(void);
 
 /* ---------------------------------------------------------------------------
  * FP8 ("SAGE") attention  ([Blog §4.3], figure 6): the same attention with Q, K, P and

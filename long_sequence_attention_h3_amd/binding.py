@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libh3attn.so")
 H3_OK = 0
 STATUS_NAMES = {0: "H3_OK", 1: "H3_ERR_NULL", 2: "H3_ERR_SHAPE", 3: "H3_ERR_ALIGN",
                 4: "H3_ERR_UNSUPPORTED", 5: "H3_ERR_DEVICE", 6: "H3_ERR_LAUNCH",
-                7: "H3_ERR_WORKSPACE"}
+                7: "H3_ERR_WORKSPACE", 8: "H3_ERR_SCRATCH_LIMIT"}
 
 
 class H3Error(RuntimeError):
@@ -61,7 +61,8 @@ def make_rope(theta: float, n_1d: int, sections=(0, 0, 0), grid=(0, 0, 0)) -> Ro
 EXPORTED = ("h3_status_string", "h3_version", "h3_qk_rmsnorm_rope", "h3_attn_workspace_size",
             "h3_kv_pack", "h3_attn_packed", "h3_attn_varlen", "h3_attn_layer",
             "h3_attn_fp8_workspace_size", "h3_kv_pack_fp8", "h3_attn_packed_fp8",
-            "h3_attn_varlen_fp8", "h3_attn_layer_fp8", "h3_residual_norm_modulate")
+            "h3_attn_varlen_fp8", "h3_attn_layer_fp8", "h3_residual_norm_modulate",
+            "h3_attn_layer_noalloc", "h3_attn_layer_noalloc_max_workspace")
 
 _lib = None
 
@@ -93,6 +94,10 @@ def lib():
         L.h3_attn_varlen.restype = ctypes.c_int
         L.h3_attn_layer.argtypes = [P, P, P, P, P, P, I64, F, RP, F, SH, P, SZ, P]
         L.h3_attn_layer.restype = ctypes.c_int
+        L.h3_attn_layer_noalloc.argtypes = [P, P, P, P, P, P, I64, F, RP, F, SH, P]
+        L.h3_attn_layer_noalloc.restype = ctypes.c_int
+        L.h3_attn_layer_noalloc_max_workspace.argtypes = []
+        L.h3_attn_layer_noalloc_max_workspace.restype = SZ
         L.h3_attn_fp8_workspace_size.argtypes = [SH]
         L.h3_attn_fp8_workspace_size.restype = SZ
         L.h3_kv_pack_fp8.argtypes = [P, P, P, I64, F, RP, SH, P, SZ, P]
@@ -281,6 +286,30 @@ def attn_layer(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_scale
                                ctypes.byref(call.shape), _p(ws), _nbytes(ws),
                                ctypes.c_void_p(st)), "h3_attn_layer")
     return out
+
+
+def attn_layer_noalloc(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope,
+                       softmax_scale: float, out, stream=None):
+    """h3_attn_layer with the library's static scratch as its workspace
+    (h3_attn_layer_noalloc): the call allocates nothing; ``out`` must be given."""
+    if out is None:
+        raise ValueError("attn_layer_noalloc allocates nothing: pass out")
+    s_in, out, s_out = _qkv_strides(q, k, v, out)
+    if w_q is None or w_k is None:
+        raise ValueError("w_q and w_k are required")
+    w_head_stride = _weight_stride(q, w_q, w_k)
+    call = _Call(q, n_valid, s_in, s_out)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_layer_noalloc(_p(q), _p(k), _p(v), _p(out), _p(w_q), _p(w_k),
+                                       w_head_stride, float(eps), ctypes.byref(rope),
+                                       float(softmax_scale), ctypes.byref(call.shape),
+                                       ctypes.c_void_p(st)), "h3_attn_layer_noalloc")
+    return out
+
+
+def noalloc_max_workspace() -> int:
+    """Bytes of the static scratch behind attn_layer_noalloc."""
+    return int(lib().h3_attn_layer_noalloc_max_workspace())
 
 
 def kv_pack(k, v, n_valid, workspace=None, w_k=None, eps: float = 0.0, rope: Rope | None = None,

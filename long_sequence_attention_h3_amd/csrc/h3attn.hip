@@ -14,6 +14,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "attention.hpp"
 #include "attention_fp8.hpp"
@@ -386,6 +387,31 @@ h3_status do_attn_packed_fp8(const void* q, void* o, const void* w_q, int64_t w_
   return H3_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free entry
+// Workspace of h3_attn_layer_noalloc: a static device array, one per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address is used.
+constexpr size_t kScratchBytes = size_t(64) << 20;  // 64 MiB
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// This device's address of `scratch` (looked up on the first call on the device).
+h3_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return H3_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return H3_ERR_DEVICE;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return H3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -400,6 +426,9 @@ const char* h3_status_string(h3_status s) {
     case H3_ERR_DEVICE: return "H3_ERR_DEVICE: no current gfx950 device";
     case H3_ERR_LAUNCH: return "H3_ERR_LAUNCH: kernel launch failed";
     case H3_ERR_WORKSPACE: return "H3_ERR_WORKSPACE: workspace missing or too small";
+    case H3_ERR_SCRATCH_LIMIT:
+      return "H3_ERR_SCRATCH_LIMIT: the problem needs more workspace than the static "
+             "scratch of the allocation-free entry point holds";
   }
   return "unknown h3_status";
 }
@@ -492,6 +521,25 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
                     workspace_bytes_, stream));
   return do_attn_packed(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape, workspace,
                         workspace_bytes_, stream);
+}
+
+size_t h3_attn_layer_noalloc_max_workspace(void) { return kScratchBytes; }
+
+h3_status h3_attn_layer_noalloc(const void* q, const void* k, const void* v, void* o,
+                                const void* w_q, const void* w_k, int64_t w_head_stride,
+                                float eps, const h3_rope* rope, float softmax_scale,
+                                const h3_shape* shape, hipStream_t stream) {
+  int64_t max_valid = 0;
+  H3_TRY(check_shape(shape, &max_valid));
+  if (workspace_bytes(shape) > kScratchBytes) return H3_ERR_SCRATCH_LIMIT;
+  H3_TRY(check_device());
+  void* ws = nullptr;
+  H3_TRY(scratch_address(&ws));
+  // The same two stages as h3_attn_layer, with the static scratch as their workspace.
+  // Nothing in it needs clearing: kv_pack writes every tile image the attention reads,
+  // and the fast pass writes every pass flag before the checked pass reads it.
+  return h3_attn_layer(q, k, v, o, w_q, w_k, w_head_stride, eps, rope, softmax_scale, shape,
+                       ws, kScratchBytes, stream);
 }
 
 size_t h3_attn_fp8_workspace_size(const h3_shape* shape) {
