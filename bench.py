@@ -30,9 +30,13 @@ inputs already resident in HBM.  Prints one JSON line:
   sclk_mhz   the shader clock the driver reported right after the timed region
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-       python bench.py --only attn   (K/V pre-pass once, then K attention launches only:
-                                      the run the hardware counters are read from)
+       python bench.py --only attn   (K/V pre-pass once, then one untimed and K timed
+                                      attention launches only, with a JSON line of their
+                                      HIP-event time: the run the kernel trace and the
+                                      hardware counters are read from)
        python bench.py --only attn_fp8  (the same for the FP8 attention kernel)
+       python bench.py --only prologue  (K launches each of the standalone prologue and
+                                      the K/V pre-pass, timed the same way)
        python bench.py --only copy   (K copies of a 2 GiB buffer: a plain copy kernel of
                                       known size that calibrates those counters)
 """
@@ -273,7 +277,8 @@ def main() -> int:
     ap.add_argument("--no-large-scores", action="store_true",
                     help="skip the checked-pass measurement (keeps a kernel trace to the "
                          "headline's launches)")
-    ap.add_argument("--only", choices=("all", "attn", "attn_fp8", "copy"), default="all")
+    ap.add_argument("--only", choices=("all", "attn", "attn_fp8", "prologue", "copy"),
+                    default="all")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the layer is "
@@ -310,22 +315,61 @@ def main() -> int:
         B.attn_layer(d["q"], d["k"], d["v"], d["w_q"], d["w_k"], n, w.eps, rope, scale,
                      out=out, workspace=ws)
 
+    def launches(name, fn, nbytes=None, flop=None):
+        """One untimed call, then args.steps calls bracketed by HIP events on the launch
+        stream; prints one JSON line of their average time."""
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn()
+            log(f"[bench] {name} launch {i + 1}/{args.steps} issued")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        rec = {"only": name, "workload": w.name, "launches_timed": args.steps,
+               "launches_total": args.steps + 1, "ms_per_launch": round(ms, 4),
+               "sclk_mhz": sclk_mhz(), "source_hash": source_hash(FP8_KERNEL_SOURCES)}
+        if flop is not None:
+            rec["tflops"] = round(flop / ms / 1e9, 2)
+            rec["frac_bf16_peak"] = round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+        if nbytes is not None:
+            rec["bytes"] = nbytes
+            rec["GB/s"] = round(nbytes / ms / 1e6, 1)
+        return rec
+
     if args.only == "attn":
         B.kv_pack(d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps, rope=rope,
                   softmax_scale=scale)
-        for i in range(args.steps):
-            B.attn_packed(d["q"], ws, n, scale, w_q=d["w_q"], eps=w.eps, rope=rope, out=out)
-            torch.cuda.synchronize()
-            log(f"[bench] attention launch {i + 1}/{args.steps} done")
+        rec = launches("attn", lambda: B.attn_packed(d["q"], ws, n, scale, w_q=d["w_q"],
+                                                     eps=w.eps, rope=rope, out=out),
+                       flop=w.flops)
+        rec["kernels"] = "attn_fwd_kernel fast pass + checked pass per launch"
+        print(json.dumps(rec), flush=True)
         return 0
     if args.only == "attn_fp8":
         ws8 = torch.empty(B.workspace_size(d["q"], fp8=True), dtype=torch.uint8, device=dev)
         B.kv_pack_fp8(d["k"], d["v"], n, workspace=ws8, w_k=d["w_k"], eps=w.eps, rope=rope)
-        for i in range(args.steps):
-            B.attn_packed_fp8(d["q"], ws8, n, scale, w_q=d["w_q"], eps=w.eps, rope=rope,
-                              out=out)
-            torch.cuda.synchronize()
-            log(f"[bench] fp8 attention launch {i + 1}/{args.steps} done")
+        rec = launches("attn_fp8", lambda: B.attn_packed_fp8(d["q"], ws8, n, scale,
+                                                             w_q=d["w_q"], eps=w.eps,
+                                                             rope=rope, out=out),
+                       flop=w.flops)
+        rec["frac_fp8_peak"] = round(rec["tflops"] / PEAK_FP8_TFLOPS, 4)
+        print(json.dumps(rec), flush=True)
+        return 0
+    if args.only == "prologue":
+        row_bytes = w.heads * w.head_dim * 2
+        q2, k2 = torch.empty_like(d["q"]), torch.empty_like(d["k"])
+        recs = [launches("qk_norm_rope_kernel", lambda: B.qk_rmsnorm_rope(
+            d["q"], d["k"], d["w_q"], d["w_k"], n, w.eps, rope, q_out=q2, k_out=k2),
+            nbytes=2 * 2 * w.n_valid * row_bytes)]
+        tiles = (w.n_valid + 63) // 64
+        recs.append(launches("kv_pack_kernel", lambda: B.kv_pack(
+            d["k"], d["v"], n, workspace=ws, w_k=d["w_k"], eps=w.eps, rope=rope,
+            softmax_scale=scale), nbytes=2 * w.n_valid * row_bytes + w.heads * tiles * 35840))
+        for r in recs:
+            print(json.dumps(r), flush=True)
         return 0
 
     # ---- parity first: the first h3_attn_layer call against the fp64 oracle on sampled

@@ -84,7 +84,8 @@ def test_bench_refuses_to_report_a_value_when_parity_fails():
     src = inspect.getsource(bench.main)
     check_at = src.index("check = oracle_check(")
     refuse_at = src.index("print(refusal(w, check)")
-    assert check_at < refuse_at < src.index("e0.record(stream)")
+    headline = src.index("# ---- headline: K whole-layer steps")
+    assert check_at < refuse_at < headline < src.index("e0.record(stream)", headline)
     assert "return 1" in src[refuse_at:refuse_at + 80]
 
 
