@@ -464,7 +464,7 @@ def main() -> int:
         ms_big = timed(lambda: B.attn_layer(d["q"], d["k"], d["v"], w_q6, w_k6, n, w.eps, rope,
                                             scale, out=out, workspace=ws), args.steps)
         valid_blocks = (w.n_valid + 255) // 256
-        big_checked = float(B.pass_flags(ws, d["q"])[:, :, :valid_blocks].float().mean())
+        big_checked = float(B.pass_flags(ws, d["q"], n)[..., :valid_blocks].float().mean())
         large_scores = {"weights": "w_q, w_k x 6", "ms_per_step": round(ms_big, 4),
                         "tflops": round(flops / ms_big / 1e9, 2),
                         "workgroups_in_checked_pass": round(big_checked, 4)}

@@ -194,6 +194,12 @@ h3_status h3_attn_layer_noalloc(const void* q, const void* k, const void* v, voi
                                 float eps, const h3_rope* rope, float softmax_scale,
                                 const h3_shape* shape, hipStream_t stream);
 
+/* Key ranges each 256-row query block of batch `batch` is split into by the attention
+ * calls (1: none; 0 for an invalid shape or batch).  Grids of few rounds on the chip's
+ * compute units split the keys so that every unit stays busy; the ranges' partial
+ * results are combined in a fixed order, so results stay deterministic. */
+int h3_attn_splits(const h3_shape* shape, int batch);
+
 /* Bytes of the static scratch behind h3_attn_layer_noalloc (the largest
  * h3_attn_workspace_size it accepts). */
 size_t h3_attn_layer_noalloc_max_workspace(void);

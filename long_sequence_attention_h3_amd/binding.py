@@ -62,7 +62,7 @@ EXPORTED = ("h3_status_string", "h3_version", "h3_qk_rmsnorm_rope", "h3_attn_wor
             "h3_kv_pack", "h3_attn_packed", "h3_attn_varlen", "h3_attn_layer",
             "h3_attn_fp8_workspace_size", "h3_kv_pack_fp8", "h3_attn_packed_fp8",
             "h3_attn_varlen_fp8", "h3_attn_layer_fp8", "h3_residual_norm_modulate",
-            "h3_attn_layer_noalloc", "h3_attn_layer_noalloc_max_workspace")
+            "h3_attn_layer_noalloc", "h3_attn_layer_noalloc_max_workspace", "h3_attn_splits")
 
 _lib = None
 
@@ -86,6 +86,8 @@ def lib():
         L.h3_qk_rmsnorm_rope.restype = ctypes.c_int
         L.h3_attn_workspace_size.argtypes = [SH]
         L.h3_attn_workspace_size.restype = SZ
+        L.h3_attn_splits.argtypes = [SH, ctypes.c_int]
+        L.h3_attn_splits.restype = ctypes.c_int
         L.h3_kv_pack.argtypes = [P, P, P, I64, F, RP, F, SH, P, SZ, P]
         L.h3_kv_pack.restype = ctypes.c_int
         L.h3_attn_packed.argtypes = [P, P, P, I64, F, RP, F, SH, P, SZ, P]
@@ -211,10 +213,13 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def workspace_size(x: torch.Tensor, fp8: bool = False) -> int:
+def workspace_size(x: torch.Tensor, fp8: bool = False, n_valid=None) -> int:
     """Workspace bytes an attention call on a tensor shaped like ``x`` needs (``fp8``:
-    the FP8 calls)."""
-    c = _Call(x, 0, x.shape[-2] * x.shape[-1], x.shape[-2] * x.shape[-1])
+    the FP8 calls) for valid lengths ``n_valid`` (int or one per batch; default the
+    buffer length S, which bounds the need of every N <= S)."""
+    _, S, _, _ = _dims(x)
+    c = _Call(x, S if n_valid is None else n_valid, x.shape[-2] * x.shape[-1],
+              x.shape[-2] * x.shape[-1])
     f = lib().h3_attn_fp8_workspace_size if fp8 else lib().h3_attn_workspace_size
     return int(f(ctypes.byref(c.shape)))
 
@@ -439,16 +444,31 @@ def attn_packed_fp8(q, workspace, n_valid, softmax_scale: float, w_q=None, eps: 
     return out
 
 
-def pass_flags(workspace, x: torch.Tensor) -> torch.Tensor:
-    """Which pass handled each 256-row workgroup in the last bf16 attention call with
-    ``workspace`` for a tensor shaped like ``x``: [B, H, ceil(S / 256)] int32, 0 = the
-    fast pass (scores provably bounded), 1 = the checked pass (layout documented with
-    h3_attn_workspace_size)."""
+def attn_splits(x: torch.Tensor, n_valid=None) -> list:
+    """Key ranges per 256-row query block the bf16 attention calls use for each batch of
+    a tensor shaped like ``x`` with valid lengths ``n_valid`` (default S)
+    (h3_attn_splits)."""
     B, S, H, D = _dims(x)
+    c = _Call(x, S if n_valid is None else n_valid, H * D, H * D)
+    return [int(lib().h3_attn_splits(ctypes.byref(c.shape), b)) for b in range(B)]
+
+
+def pass_flags(workspace, x: torch.Tensor, n_valid=None) -> torch.Tensor:
+    """Which pass handled each workgroup in the last bf16 attention call with
+    ``workspace`` for a tensor shaped like ``x`` with valid lengths ``n_valid`` (default
+    S): [B, H, k, ceil(S / 256)] int32 for k key ranges per 256-row block (the same for
+    every batch), 0 = the fast pass (scores provably bounded), 1 = the checked pass
+    (layout documented with h3_attn_workspace_size)."""
+    B, S, H, D = _dims(x)
+    ks = attn_splits(x, n_valid)
+    if len(set(ks)) != 1:
+        raise ValueError(f"batches split their keys differently: {ks}")
+    k = ks[0]
     img = B * H * ((S + 63) // 64) * 35840
     blocks = (S + 255) // 256
-    n = B * H * blocks
-    return workspace[img: img + 4 * n].view(torch.int32).view(B, H, blocks)
+    per_batch = 8 * H * blocks  # flag words per batch (up to 8 key ranges)
+    words = workspace[img: img + 4 * B * per_batch].view(torch.int32).view(B, per_batch)
+    return words[:, : k * H * blocks].reshape(B, H, k, blocks)
 
 
 def fp8_skip_counts(workspace, x: torch.Tensor) -> torch.Tensor:

@@ -78,6 +78,14 @@ struct AttnArgs {
   int m_tiles;            // ceil(seq_buf / rows per workgroup)
   float scale_log2;       // softmax_scale * log2(e)
   int* wg_checked;        // per workgroup: 1 = left to the checked pass
+  // Key ranges per query block.  1: each workgroup takes every key and writes O.  k > 1:
+  // workgroup (head, split, block) takes tiles [nt*split/k, nt*(split+1)/k) and writes
+  // its unnormalised O (fp32, part + ((split*heads + head)*seq_buf + row)*128) and its
+  // running maximum (log2 units) and row sum (part_ml, same index times 2);
+  // attn_merge_kernel combines them.
+  int splits;
+  float* part;
+  float* part_ml;
   // fused Q prologue
   const __bf16* w_q;
   int64_t w_head_stride;
@@ -463,8 +471,11 @@ attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSlots * kTileImageBytes];
   __shared__ FreqTable ft;
 
-  const int logical = xcd_remap(blockIdx.x, a.heads * a.m_tiles);
-  const int head = logical / a.m_tiles;
+  // logical workgroup = (head, split, query block), so the workgroups resident on one
+  // XCD stream the same key range of one head
+  const int logical = xcd_remap(blockIdx.x, a.heads * a.m_tiles * a.splits);
+  const int hs = logical / a.m_tiles;
+  const int head = hs / a.splits, split = hs % a.splits;
   const int64_t m0 = (int64_t)(logical % a.m_tiles) * kRows;
   const int tid = threadIdx.x;
   // the wave index is uniform across the wave: keep it in a scalar register
@@ -474,9 +485,9 @@ attn_fwd_kernel(AttnArgs a) {
 
   const int wg = logical;
   if (kCheck && a.wg_checked[wg] == 0) return;  // done by the fast pass
-  if (m0 >= a.n_valid) {  // rows past the valid length: zeros only
-    if (tid == 0) a.wg_checked[wg] = 0;
-    zero_rows(a, m0, kRows, head, tid, kThreads);
+  if (m0 >= a.n_valid) {  // rows past the valid length: zeros only (the merge writes
+    if (tid == 0) a.wg_checked[wg] = 0;  // them when the keys are split)
+    if (a.splits == 1) zero_rows(a, m0, kRows, head, tid, kThreads);
     return;
   }
   if (kFusedQ) {
@@ -497,9 +508,16 @@ attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) w.o[db] = f32x16{};
 
-  const int nt = (int)((a.n_valid + kTileKeys - 1) / kTileKeys);
-  const char* img = a.img + (int64_t)head * a.tiles_per_head * kTileImageBytes;
-  const int tail = (int)(a.n_valid - (int64_t)(nt - 1) * kTileKeys);  // valid keys, last tile
+  // this workgroup's key tiles [t_lo, t_hi) (all of them unless the keys are split; the
+  // host keeps splits <= tiles, so every range holds at least one tile)
+  const int nt_all = (int)((a.n_valid + kTileKeys - 1) / kTileKeys);
+  const int t_lo = (int)((int64_t)nt_all * split / a.splits);
+  const int t_hi = (int)((int64_t)nt_all * (split + 1) / a.splits);
+  const int nt = t_hi - t_lo;
+  const char* img = a.img + ((int64_t)head * a.tiles_per_head + t_lo) * kTileImageBytes;
+  // valid keys of the range's last tile
+  const int tail = t_hi == nt_all ? (int)(a.n_valid - (int64_t)(nt_all - 1) * kTileKeys)
+                                  : kTileKeys;
 
   // The factor the stored K rows carry (tile 0's pad; the same for every tile).  When it
   // is c2 itself, the scores leave the matrix cores in exp2 units: the QK accumulation
@@ -717,6 +735,21 @@ attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: lane holds O[row][d = db*32 + 8i + 4hl + j] at register 4i+j
+  if (a.splits > 1) {  // this key range's partial result; rows >= N are the merge's
+    if (row_valid) {
+      const float l = pair_sum(w.l);
+      const int64_t idx = ((int64_t)split * a.heads + head) * a.seq_buf + row;
+      float* po = a.part + idx * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(po + db * 32 + 8 * i + 4 * hl) =
+              f32x4{w.o[db][4 * i], w.o[db][4 * i + 1], w.o[db][4 * i + 2], w.o[db][4 * i + 3]};
+      if (hl == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * idx) = f32x2{w.m * w.c, l};
+    }
+    return;
+  }
   if (row < a.seq_buf) {
     const float inv = 1.0f / pair_sum(w.l);
     __bf16* orow = a.o + row * a.out_stride + hoff;
@@ -732,6 +765,51 @@ attn_fwd_kernel(AttnArgs a) {
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * i + 4 * hl) = v;
       }
   }
+}
+
+// Combines the key ranges of a split launch: per (row, head), with m_s and l_s the
+// ranges' running maxima (log2 units) and row sums and O_s their unnormalised outputs,
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, the ranges taken in
+// order (deterministic); rows in [N, S) get zeros.  16 rows x 16 chunks of 8 channels
+// per 256-thread workgroup.
+struct MergeArgs {
+  const float* part;
+  const float* part_ml;
+  __bf16* o;
+  int64_t out_stride;
+  int64_t n_valid, seq_buf;
+  int heads, splits;
+};
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int head = blockIdx.y, cc = threadIdx.x & 15;
+  if (row >= a.seq_buf) return;
+  u32x4 res = {0u, 0u, 0u, 0u};
+  if (row < a.n_valid) {
+    float mx = -INFINITY;
+    for (int s = 0; s < a.splits; ++s)
+      mx = fmaxf(mx, a.part_ml[2 * (((int64_t)s * a.heads + head) * a.seq_buf + row)]);
+    float l = 0.0f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.splits; ++s) {
+      const int64_t idx = ((int64_t)s * a.heads + head) * a.seq_buf + row;
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * idx);
+      const float f = __builtin_amdgcn_exp2f(ml[0] - mx);
+      l = __builtin_fmaf(f, ml[1], l);
+      const f32x4* po = reinterpret_cast<const f32x4*>(a.part + idx * kHeadDim + cc * 8);
+      const f32x4 lo = po[0], hi = po[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = __builtin_fmaf(f, lo[e], acc[e]);
+        acc[4 + e] = __builtin_fmaf(f, hi[e], acc[4 + e]);
+      }
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    res = pack8(acc);
+  }
+  *reinterpret_cast<u32x4*>(a.o + row * a.out_stride + (int64_t)head * kHeadDim + cc * 8) = res;
 }
 
 }  // namespace h3

@@ -98,20 +98,16 @@ __device__ __forceinline__ float pair_sum(float x) {
 // copy writes, and for the intrinsic it conservatively waits for every outstanding copy
 // before the next LDS read; the callers instead wait for their own copies explicitly
 // (s_waitcnt vmcnt) and publish them with a barrier before any lane reads the bytes.
-// M0 is a reserved register to the compiler, which ignores it in a clobber list; no
-// other code in this library uses M0, so setting it here disturbs nothing.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
+// The LDS address goes in through the "{m0}" operand constraint: the compiler itself
+// writes M0 before the copy and knows that the copy reads it, so no M0 value the
+// compiler keeps live elsewhere can be disturbed.
 __device__ __forceinline__ void dma_to_lds16(const void* sbase, uint32_t voff,
                                              uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(sbase), "s"(lds_base)
-      : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "{m0}"(lds_base)
+               : "memory");
 }
-#pragma clang diagnostic pop
 
 // Workgroup -> logical tile.  Consecutive workgroup ids are dispatched round-robin over
 // the 8 XCDs; this bijection hands each XCD one contiguous range of logical tiles, so

@@ -110,16 +110,65 @@ int64_t attn_workgroups(const h3_shape* s) {
   return (int64_t)s->num_heads * ((s->seq_buf + kBM - 1) / kBM);
 }
 
-// Workspace layout: packed K/V tile images, [batch][head][tile] x kTileImageBytes, then
-// one int per attention workgroup and batch (which pass handles it).
+// Key ranges per query block.  A launch takes ceil(W / CUs) rounds of equally long
+// workgroups for W workgroups (one resident per compute unit), so a grid of few rounds
+// loses much of its last one: the 6-head, 58,816-row layer has 1,380 workgroups, 5.4
+// rounds on 256 compute units.  Splitting each block's keys into k ranges (merged by
+// attn_merge_kernel) gives ceil(k W / CUs) rounds of 1/k the length.  The k in 1..8
+// (at most the number of key tiles) with the least ceil(k W / CUs) / k * (1 + 0.02 (k-1))
+// is taken (the last factor prices the merge and each range's own start-up); ties go
+// to the smaller k.  The compute-unit count is gfx950's (MI355X); it only steers the
+// schedule, never the result's correctness.
+constexpr int kMaxSplits = 8;
+constexpr int kComputeUnits = 256;
+
+int attn_splits(const h3_shape* s, int64_t n) {
+  const int64_t W = attn_workgroups(s);
+  const int64_t nt = (n + kTileKeys - 1) / kTileKeys;
+  int best = 1;
+  double best_cost = (double)((W + kComputeUnits - 1) / kComputeUnits);
+  for (int k = 2; k <= kMaxSplits && k <= nt; ++k) {
+    const double cost = (double)((k * W + kComputeUnits - 1) / kComputeUnits) / k *
+                        (1.0 + 0.02 * (k - 1));
+    if (cost < best_cost) {
+      best = k;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+int max_splits(const h3_shape* s) {
+  int k = 1;
+  for (int b = 0; b < s->batch; ++b) {
+    const int kb = attn_splits(s, s->seq_valid[b]);
+    if (kb > k) k = kb;
+  }
+  return k;
+}
+
+// Workspace layout: packed K/V tile images, [batch][head][tile] x kTileImageBytes; then
+// one int per attention workgroup (which pass handles it), [batch][kMaxSplits x W] with
+// workgroup (head, split, block) at (head * k + split) * blocks + block; then, when some
+// batch splits its keys, the partial results of one batch (reused batch after batch):
+// O as [k][head][row][128] floats, then (m, l) as [k][head][row][2] floats.
 size_t batch_ws_bytes(const h3_shape* s) {
   return (size_t)s->num_heads * (size_t)tiles_per_head(s) * (size_t)kTileImageBytes;
 }
 size_t flags_bytes(const h3_shape* s) {
-  return ((size_t)s->batch * (size_t)attn_workgroups(s) * sizeof(int) + 255) & ~size_t(255);
+  return ((size_t)s->batch * kMaxSplits * (size_t)attn_workgroups(s) * sizeof(int) + 255) &
+         ~size_t(255);
+}
+size_t part_rows(const h3_shape* s) {
+  const int k = max_splits(s);
+  return k > 1 ? (size_t)k * (size_t)s->num_heads * (size_t)s->seq_buf : 0;
+}
+size_t part_o_bytes(const h3_shape* s) { return part_rows(s) * kHeadDim * sizeof(float); }
+size_t part_bytes(const h3_shape* s) {
+  return part_o_bytes(s) + ((part_rows(s) * 2 * sizeof(float) + 255) & ~size_t(255));
 }
 size_t workspace_bytes(const h3_shape* s) {
-  return (size_t)s->batch * batch_ws_bytes(s) + flags_bytes(s);
+  return (size_t)s->batch * batch_ws_bytes(s) + flags_bytes(s) + part_bytes(s);
 }
 
 h3_status launched() { return hipGetLastError() == hipSuccess ? H3_OK : H3_ERR_LAUNCH; }
@@ -239,11 +288,18 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
   if (S == 0) return H3_OK;
   const int m_tiles = (int)((S + kBM - 1) / kBM);
   const size_t per_batch = batch_ws_bytes(shp);
-  int* flags = reinterpret_cast<int*>(static_cast<char*>(workspace) + shp->batch * per_batch);
+  char* after_images = static_cast<char*>(workspace) + shp->batch * per_batch;
+  int* flags = reinterpret_cast<int*>(after_images);
+  float* part = reinterpret_cast<float*>(after_images + flags_bytes(shp));
+  float* part_ml = reinterpret_cast<float*>(after_images + flags_bytes(shp) + part_o_bytes(shp));
   for (int b = 0; b < shp->batch; ++b) {
     const char* ws = static_cast<const char*>(workspace) + b * per_batch;
+    const int splits = attn_splits(shp, shp->seq_valid[b]);
     AttnArgs aa{};
-    aa.wg_checked = flags + b * attn_workgroups(shp);
+    aa.wg_checked = flags + (size_t)b * kMaxSplits * attn_workgroups(shp);
+    aa.splits = splits;
+    aa.part = part;
+    aa.part_ml = part_ml;
     aa.q = static_cast<const __bf16*>(q) + b * S * shp->in_row_stride;
     aa.o = static_cast<__bf16*>(o) + b * S * shp->out_row_stride;
     aa.img = ws;
@@ -259,7 +315,7 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
     aa.w_head_stride = w_head_stride;
     aa.eps = eps;
     aa.rope = ra;
-    const unsigned blocks = (unsigned)((int64_t)H * m_tiles);
+    const unsigned blocks = (unsigned)((int64_t)H * m_tiles * splits);
     // fast pass, then the checked pass for the workgroups the fast pass flagged
     if (norm) {
       attn_fwd_kernel<true, false><<<blocks, attn::kThreads, 0, stream>>>(aa);
@@ -269,6 +325,19 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
       attn_fwd_kernel<false, true><<<blocks, attn::kThreads, 0, stream>>>(aa);
     }
     H3_TRY(launched());
+    if (splits > 1) {
+      MergeArgs ma{};
+      ma.part = part;
+      ma.part_ml = part_ml;
+      ma.o = aa.o;
+      ma.out_stride = aa.out_stride;
+      ma.n_valid = aa.n_valid;
+      ma.seq_buf = S;
+      ma.heads = H;
+      ma.splits = splits;
+      attn_merge_kernel<<<dim3((unsigned)((S + 15) / 16), (unsigned)H), 256, 0, stream>>>(ma);
+      H3_TRY(launched());
+    }
   }
   return H3_OK;
 }
@@ -540,6 +609,12 @@ h3_status h3_attn_layer_noalloc(const void* q, const void* k, const void* v, voi
   // and the fast pass writes every pass flag before the checked pass reads it.
   return h3_attn_layer(q, k, v, o, w_q, w_k, w_head_stride, eps, rope, softmax_scale, shape,
                        ws, kScratchBytes, stream);
+}
+
+int h3_attn_splits(const h3_shape* shape, int batch) {
+  int64_t max_valid = 0;
+  if (check_shape(shape, &max_valid) != H3_OK || batch < 0 || batch >= shape->batch) return 0;
+  return attn_splits(shape, shape->seq_valid[batch]);
 }
 
 size_t h3_attn_fp8_workspace_size(const h3_shape* shape) {

@@ -69,21 +69,50 @@ def prologue(s, r, q_out=FAKE, eps=1e-6):
 
 
 def test_workspace_size_formula():
+    """Tile images, then 8 pass-flag words per 256 query rows and head (room for up to 8
+    key ranges) per batch, then, when some batch splits its keys into k > 1 ranges, the
+    partial results of one batch: k*H*S rows of 128 floats, then k*H*S (max, sum) pairs."""
     L = B.lib()
     tile = 64 * 272 + 128 * 144  # padded K rows + padded V rows per 64-key tile
 
-    def flags(words):  # one int per 256 query rows, rounded up to 256 bytes
-        return (words * 4 + 255) // 256 * 256
+    def r256(nbytes):
+        return (nbytes + 255) // 256 * 256
+
+    def flags(words):
+        return r256(words * 4)
+
+    def part(k, H, S):
+        return k * H * S * 128 * 4 + r256(k * H * S * 2 * 4)
 
     assert tile == 35840
     assert L.h3_attn_workspace_size(ctypes.byref(shape(H=42, S=58816, valid=(58758,)))) == \
-        42 * 919 * tile + flags(42 * 230)
+        42 * 919 * tile + flags(8 * 42 * 230)
+    assert L.h3_attn_workspace_size(ctypes.byref(shape(H=6, S=58816, valid=(58758,)))) == \
+        6 * 919 * tile + flags(8 * 6 * 230) + part(2, 6, 58816)
+    assert L.h3_attn_workspace_size(ctypes.byref(shape(H=2, S=1024, valid=(1000,)))) == \
+        2 * 16 * tile + flags(8 * 2 * 4) + part(8, 2, 1024)
     assert L.h3_attn_workspace_size(ctypes.byref(shape(S=65, valid=(1,)))) == \
-        2 * 2 * tile + flags(2 * 1)
+        2 * 2 * tile + flags(8 * 2 * 1)
     assert L.h3_attn_workspace_size(ctypes.byref(shape(B_=3, S=64, valid=(1, 2, 3)))) == \
-        3 * 2 * 1 * tile + flags(3 * 2 * 1)
+        3 * 2 * 1 * tile + flags(3 * 8 * 2 * 1)
     assert L.h3_attn_workspace_size(ctypes.byref(shape(D=64))) == 0
     assert L.h3_attn_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("H,S,N,k", [
+    (2, 1024, 1000, 8),     # 8 query blocks: 8 key ranges of 2 tiles
+    (8, 8192, 8150, 1),     # 256 blocks: one round on 256 compute units
+    (6, 58816, 58758, 2),   # 1,380 blocks, 5.4 rounds: 2 ranges, 10.8 rounds
+    (42, 58816, 58758, 1),  # 9,660 blocks, 37.7 rounds
+    (42, 87552, 87500, 1),
+    (2, 1024, 64, 1),       # one key tile cannot be split
+    (2, 1024, 65, 2),
+])
+def test_key_range_splits(H, S, N, k):
+    L = B.lib()
+    assert L.h3_attn_splits(ctypes.byref(shape(H=H, S=S, valid=(N,))), 0) == k
+    assert L.h3_attn_splits(ctypes.byref(shape(H=H, S=S, valid=(N,))), 1) == 0  # no batch 1
+    assert L.h3_attn_splits(ctypes.byref(shape(D=64)), 0) == 0
 
 
 @pytest.mark.parametrize("kwargs,code", [

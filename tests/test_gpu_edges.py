@@ -165,11 +165,13 @@ def test_large_scores_mix_both_passes(dev):
     say("[edge] large scores, varlen")
     ws = torch.empty(B.workspace_size(d["q"]), dtype=torch.uint8, device=dev)
     out = gpu_varlen(w, d, workspace=ws)
-    # rows [256, 512) of both heads were left to the checked pass, every other workgroup
-    # was finished by the fast pass
-    flags = B.pass_flags(ws, d["q"]).cpu()
+    # rows [256, 512) of both heads were left to the checked pass in every key range,
+    # every other workgroup was finished by the fast pass (this grid of 12 query blocks
+    # splits its keys into several ranges)
+    flags = B.pass_flags(ws, d["q"], n).cpu()
+    assert flags.shape[2] == B.attn_splits(d["q"], n)[0] > 1
     want = torch.zeros_like(flags)
-    want[:, :, 1] = 1
+    want[:, :, :, 1] = 1
     assert torch.equal(flags, want), flags
     assert_tail_zero(out, [n], "large scores varlen")
     rows = list(range(n))

@@ -180,10 +180,13 @@ def test_tail_contents_never_matter(cfg, dev):
         assert torch.equal(o, outs[1])
 
 
-def test_deterministic_run_to_run(dev):
-    w = W.WORKLOADS[1]
-    d = to_dev(inputs(1), dev)
-    say("[determinism] workload 1")
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_deterministic_run_to_run(cfg, dev):
+    """Bit-identical outputs run to run, also where the keys are split into ranges whose
+    partial results are merged (the 6-head share: 2 ranges per query block)."""
+    w = W.WORKLOADS[cfg]
+    d = to_dev(inputs(cfg), dev)
+    say(f"[determinism] workload {cfg}, key ranges {B.attn_splits(d['q'], w.n_valid)}")
     a = gpu_layer(w, d).view(torch.int16).clone()
     for _ in range(2):
         assert torch.equal(gpu_layer(w, d).view(torch.int16), a)
