@@ -164,7 +164,9 @@ h3_status h3_attn_varlen(const void* q, const void* k, const void* v, void* o,
                          float softmax_scale, const h3_shape* shape, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
-/* The whole layer: per-head Q/K RMSNorm + RoPE fused into the attention prologue,
+/* The whole layer ([Blog §3.1]: attention over the valid tokens of an aligned packed
+ * buffer, RoPE rows built per token; [Blog §3.2]: Q/K RMSNorm and RoPE as one fused
+ * operator): per-head Q/K RMSNorm + RoPE fused into the attention prologue,
  * then attention as in h3_attn_varlen, with normalised Q and K never round-tripping
  * through a bf16 [S, H, D] buffer: K is prepared once into the workspace (h3_kv_pack
  * with w_k, which stores it times softmax_scale * log2(e), rounded once), Q in registers
@@ -209,8 +211,8 @@ size_t h3_attn_layer_noalloc_max_workspace(void);
  * V quantized to FP8 E4M3 (OCP "fn": largest finite 448, round to nearest even) for
  * both products on the FP8 matrix cores.  The quantization groups (the reading of
  * "K16"): one scale per Q row, per block of 16 consecutive keys, and per V channel over
- * the N_b valid tokens, each per head; a group's scale is amax / 448, every element is
- * multiplied by 448 / amax in fp32, clamped to +-448 and rounded.  The softmax weights
+ * the N_b valid tokens, each per head; a group's scale is amax / 448 and an element's
+ * code is the E4M3 rounding of the exact x * 448 / amax.  The softmax weights
  * are those of a streaming softmax over 64-key tiles: P = E4M3(256 exp(s - m_t)) with
  * m_t the running row maximum through the key's tile, earlier sums carried over by
  * exp(m_(t-1) - m_t); each row is normalised by the sum of its quantized weights.
