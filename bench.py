@@ -20,6 +20,8 @@ inputs already resident in HBM.  Prints one JSON line:
              fp8.skip_softmax: the same step with Skip-Softmax (threshold 0.01) on these
              inputs and on frame-local inputs of the same shape, with the share of wave
              tiles skipped and the dense bf16 / dense FP8 times on those inputs
+  skip_softmax_only  the Skip-Softmax-only control (h3_attn_layer_skip: dense bf16 with
+             tile skipping, threshold 0.01) on these and on the frame-local inputs
   per_workload  every workload size: h3_attn_layer and h3_attn_varlen TFLOP/s (median and
              min of 10 calls after 3 warm-up calls), the same for the FP8 calls,
              h3_qk_rmsnorm_rope GB/s, and (unless --no-cpu-baseline) `oracle`: the fp64
@@ -541,6 +543,29 @@ def main() -> int:
         f"frame-local bf16 {ms_bf16_local:.3f} ms, fp8 dense {dense_local['ms_per_step']} ms, "
         f"fp8 skip {skip_local['ms_per_step']} ms ({100 * skip_local['wave_tiles_skipped']:.1f} % "
         f"of wave tiles skipped)")
+
+    # ---- the Skip-Softmax-only control: dense bf16 attention with Skip-Softmax, on these
+    # inputs and on the frame-local ones, against dense bf16 on the same inputs
+    def bf16_skip_run(dd, lam):
+        ms = timed(lambda: B.attn_layer_skip(dd["q"], dd["k"], dd["v"], dd["w_q"], dd["w_k"], n,
+                                             w.eps, rope, scale, lam, out=out, workspace=ws),
+                   args.steps)
+        skipped = int(B.skip_counts(ws, dd["q"]).sum())
+        return {"ms_per_step": round(ms, 4), "tflops_equiv": round(flops / ms / 1e9, 2),
+                "wave_tiles_skipped": round(skipped / wave_tiles, 4)}
+
+    skip_only = {"threshold": SKIP_LAMBDA, "entry": "h3_attn_layer_skip",
+                 "rule": skip["rule"] + " (dense bf16, exact running max of the kept tiles)",
+                 "this_workload": bf16_skip_run(d, SKIP_LAMBDA),
+                 "this_workload_bf16_dense_ms": round(ms_step, 4)}
+    sk_local = bf16_skip_run(dl, SKIP_LAMBDA)
+    skip_only["frame_local"] = {"bf16_dense_ms": round(ms_bf16_local, 4), "bf16_skip": sk_local,
+                                "speedup_over_bf16_dense": round(ms_bf16_local /
+                                                                 sk_local["ms_per_step"], 3)}
+    log(f"[bench] skip-softmax-only (bf16) {SKIP_LAMBDA}: this workload "
+        f"{skip_only['this_workload']}; frame-local {sk_local['ms_per_step']} ms "
+        f"({100 * sk_local['wave_tiles_skipped']:.1f} % of wave tiles skipped) vs dense "
+        f"{ms_bf16_local:.3f} ms")
     del ws8, out8, dl
 
     # ---- DiT block steps around attention: gated residual + LayerNorm + modulation on the
@@ -602,6 +627,7 @@ def main() -> int:
                 "frac_hbm": round(blk0_bytes / ms_blk0 / 1e6 / PEAK_HBM_GBS, 4)},
         },
         "fp8": fp8,
+        "skip_softmax_only": skip_only,
         "wall_s_timed_region": round(wall, 4),
         "sclk_mhz": sclk,
         "source_hash": source_hash(),

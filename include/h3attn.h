@@ -180,6 +180,27 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
                         const h3_rope* rope, float softmax_scale, const h3_shape* shape,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Dense (bf16) attention with Skip-Softmax, the "Skip-Softmax-only" control ([Blog §4.3],
+ * figure 6: a tile-level decision from the QK result drops the softmax and P x V work of
+ * unimportant tiles; a higher threshold drops more): skip_threshold in (0, 1).  For each
+ * query row the valid keys are walked in 64-key tiles; tile t >= 1 is dropped when
+ * exp(tile maximum - running maximum of the kept tiles) < skip_threshold (scores
+ * s = softmax_scale * q . k), and the row is a softmax over the kept keys.  The result
+ * depends only on each row's own scores; work is saved where all 32 rows of a wave drop
+ * a tile.  Products and softmax as in h3_attn_varlen (its per-tile running-maximum
+ * form).  After the call, the workspace's pass-flag word of each 256-row workgroup
+ * (layout at h3_attn_workspace_size) holds the number of 32-row x 64-key wave tiles it
+ * skipped.  Same arguments as h3_attn_varlen / h3_attn_layer plus skip_threshold;
+ * H3_ERR_SHAPE for a threshold outside (0, 1). */
+h3_status h3_attn_varlen_skip(const void* q, const void* k, const void* v, void* o,
+                              float softmax_scale, float skip_threshold, const h3_shape* shape,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+h3_status h3_attn_layer_skip(const void* q, const void* k, const void* v, void* o,
+                             const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
+                             const h3_rope* rope, float softmax_scale, float skip_threshold,
+                             const h3_shape* shape, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* The same layer for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): h3_attn_layer with its
  * workspace in a static 64 MiB device array inside the library instead of a caller

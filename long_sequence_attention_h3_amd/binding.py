@@ -62,7 +62,8 @@ EXPORTED = ("h3_status_string", "h3_version", "h3_qk_rmsnorm_rope", "h3_attn_wor
             "h3_kv_pack", "h3_attn_packed", "h3_attn_varlen", "h3_attn_layer",
             "h3_attn_fp8_workspace_size", "h3_kv_pack_fp8", "h3_attn_packed_fp8",
             "h3_attn_varlen_fp8", "h3_attn_layer_fp8", "h3_residual_norm_modulate",
-            "h3_attn_layer_noalloc", "h3_attn_layer_noalloc_max_workspace", "h3_attn_splits")
+            "h3_attn_layer_noalloc", "h3_attn_layer_noalloc_max_workspace", "h3_attn_splits",
+            "h3_attn_varlen_skip", "h3_attn_layer_skip")
 
 _lib = None
 
@@ -96,6 +97,10 @@ def lib():
         L.h3_attn_varlen.restype = ctypes.c_int
         L.h3_attn_layer.argtypes = [P, P, P, P, P, P, I64, F, RP, F, SH, P, SZ, P]
         L.h3_attn_layer.restype = ctypes.c_int
+        L.h3_attn_varlen_skip.argtypes = [P, P, P, P, F, F, SH, P, SZ, P]
+        L.h3_attn_varlen_skip.restype = ctypes.c_int
+        L.h3_attn_layer_skip.argtypes = [P, P, P, P, P, P, I64, F, RP, F, F, SH, P, SZ, P]
+        L.h3_attn_layer_skip.restype = ctypes.c_int
         L.h3_attn_layer_noalloc.argtypes = [P, P, P, P, P, P, I64, F, RP, F, SH, P]
         L.h3_attn_layer_noalloc.restype = ctypes.c_int
         L.h3_attn_layer_noalloc_max_workspace.argtypes = []
@@ -291,6 +296,50 @@ def attn_layer(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_scale
                                ctypes.byref(call.shape), _p(ws), _nbytes(ws),
                                ctypes.c_void_p(st)), "h3_attn_layer")
     return out
+
+
+def attn_varlen_skip(q, k, v, n_valid, softmax_scale: float, skip_threshold: float, out=None,
+                     workspace=None, stream=None):
+    """Dense attention with Skip-Softmax over pre-normalised, pre-rotated Q/K
+    (h3_attn_varlen_skip); skip_threshold in (0, 1)."""
+    s_in, out, s_out = _qkv_strides(q, k, v, out)
+    call = _Call(q, n_valid, s_in, s_out)
+    ws = _workspace(q, call, workspace)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_varlen_skip(_p(q), _p(k), _p(v), _p(out), float(softmax_scale),
+                                     float(skip_threshold), ctypes.byref(call.shape), _p(ws),
+                                     _nbytes(ws), ctypes.c_void_p(st)), "h3_attn_varlen_skip")
+    return out
+
+
+def attn_layer_skip(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope, softmax_scale: float,
+                    skip_threshold: float, out=None, workspace=None, stream=None):
+    """The whole layer with dense Skip-Softmax attention (h3_attn_layer_skip)."""
+    s_in, out, s_out = _qkv_strides(q, k, v, out)
+    if w_q is None or w_k is None:
+        raise ValueError("w_q and w_k are required")
+    w_head_stride = _weight_stride(q, w_q, w_k)
+    call = _Call(q, n_valid, s_in, s_out)
+    ws = _workspace(q, call, workspace)
+    st = _stream(q.device) if stream is None else stream
+    _check(lib().h3_attn_layer_skip(_p(q), _p(k), _p(v), _p(out), _p(w_q), _p(w_k),
+                                    w_head_stride, float(eps), ctypes.byref(rope),
+                                    float(softmax_scale), float(skip_threshold),
+                                    ctypes.byref(call.shape), _p(ws), _nbytes(ws),
+                                    ctypes.c_void_p(st)), "h3_attn_layer_skip")
+    return out
+
+
+def skip_counts(workspace, x: torch.Tensor) -> torch.Tensor:
+    """Wave tiles (32 rows x 64 keys) each 256-row workgroup skipped in the last
+    h3_attn_varlen_skip / h3_attn_layer_skip call with ``workspace`` for a tensor shaped
+    like ``x``: [B, H, ceil(S / 256)] int32 (the pass-flag words of that call)."""
+    B, S, H, D = _dims(x)
+    img = B * H * ((S + 63) // 64) * 35840
+    blocks = (S + 255) // 256
+    per_batch = 8 * H * blocks
+    words = workspace[img: img + 4 * B * per_batch].view(torch.int32).view(B, per_batch)
+    return words[:, : H * blocks].reshape(B, H, blocks)
 
 
 def attn_layer_noalloc(q, k, v, w_q, w_k, n_valid, eps: float, rope: Rope,

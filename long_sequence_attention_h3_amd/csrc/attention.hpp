@@ -77,7 +77,9 @@ struct AttnArgs {
   int heads;
   int m_tiles;            // ceil(seq_buf / rows per workgroup)
   float scale_log2;       // softmax_scale * log2(e)
-  int* wg_checked;        // per workgroup: 1 = left to the checked pass
+  int* wg_checked;        // per workgroup: 1 = left to the checked pass (Skip-Softmax
+                          // launches: the wave tiles the workgroup skipped)
+  float skip_log2;        // Skip-Softmax launches: log2 of the threshold
   // Key ranges per query block.  1: each workgroup takes every key and writes O.  k > 1:
   // workgroup (head, split, block) takes tiles [nt*split/k, nt*(split+1)/k) and writes
   // its unnormalised O (fp32, part + ((split*heads + head)*seq_buf + row)*128) and its
@@ -326,11 +328,11 @@ __device__ __forceinline__ void steady_step(Wave& w, f32x16* cur, f32x16* nxt,
 // tile j, each operand read three MFMAs ahead; then (valu_block) the P operands and row
 // sums of the new scores.  One score set suffices: a tile's scores become P operands
 // before the next QK overwrites them.  kPre as in steady_step.
-template <bool kNext, bool kPre>
+template <bool kNext, bool kPre, bool kPV = true>
 __device__ __forceinline__ void mfma_block(Wave& w, f32x16* s, uint32_t kbase,
                                            uint32_t vbase) {
   constexpr int nq = kNext ? 16 : 0;
-  constexpr int n = nq + 16;
+  constexpr int n = nq + (kPV ? 16 : 0);
   bf16x8 op[32];
   auto read = [&](int i) {
     if (i < nq) {
@@ -362,6 +364,18 @@ __device__ __forceinline__ void mfma_block(Wave& w, f32x16* s, uint32_t kbase,
 template <bool kPre>
 __device__ __forceinline__ void valu_block(Wave& w, f32x16* s) {
   ex<kPre>(w, s);
+  cv(w, s);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// valu_block of the multiply-add form with this row's exp2 offset `off` (-inf: the row
+// drops the tile, so its P is exactly 0).
+__device__ __forceinline__ void valu_block_off(Wave& w, f32x16* s, float off) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      s[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], w.c, off));
   cv(w, s);
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -464,9 +478,12 @@ __device__ __forceinline__ float q_norm2(const bf16x8* q) {
 // kCheck = false: the fast pass; workgroups whose scores are not provably bounded are
 // flagged in wg_checked and left alone.  kCheck = true: the second pass; runs the flagged
 // workgroups with the per-tile running-max check and returns at once for the others.
-template <bool kFusedQ, bool kCheck>
+// kSkip (with kCheck): dense attention with Skip-Softmax, a launch of its own that runs
+// every workgroup (see skip_steps below).
+template <bool kFusedQ, bool kCheck, bool kSkip = false>
 __global__ __launch_bounds__(attn::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fwd_kernel(AttnArgs a) {
+  static_assert(kCheck || !kSkip, "Skip-Softmax runs in the checked pass's arithmetic");
   using namespace attn;
   __shared__ __attribute__((aligned(16))) char smem[kSlots * kTileImageBytes];
   __shared__ FreqTable ft;
@@ -484,7 +501,7 @@ attn_fwd_kernel(AttnArgs a) {
   const int64_t hoff = (int64_t)head * kHeadDim;
 
   const int wg = logical;
-  if (kCheck && a.wg_checked[wg] == 0) return;  // done by the fast pass
+  if (kCheck && !kSkip && a.wg_checked[wg] == 0) return;  // done by the fast pass
   if (m0 >= a.n_valid) {  // rows past the valid length: zeros only (the merge writes
     if (tid == 0) a.wg_checked[wg] = 0;  // them when the keys are split)
     if (a.splits == 1) zero_rows(a, m0, kRows, head, tid, kThreads);
@@ -707,6 +724,52 @@ attn_fwd_kernel(AttnArgs a) {
     loads_done();
     __syncthreads();
   };
+  // Skip-Softmax ([Blog] §4.3, figure 6: a tile-level decision from the QK result drops
+  // the softmax and P V work of unimportant tiles): tile t >= 1 is dropped for a row when
+  // exp(tile max - running max of the kept tiles) < threshold.  The checked pass's
+  // arithmetic with, besides its lazy running max (the exp2 reference), the exact running
+  // max of the kept tiles for the decision; a dropping row gets P = 0 for the tile
+  // (exp2 offset -inf) and keeps its maxima.  Every wave runs the MFMA-first step, whose
+  // VALU block and PV products stand apart from the QK products: when all 32 rows of a
+  // wave drop a tile, the wave skips that tile's VALU block and its 16 PV MFMAs.  Rows
+  // >= N always drop, so they never hold a wave back.
+  uint32_t skipped = 0;  // wave tiles this wave skipped
+  auto skip_steps = [&]() __attribute__((always_inline)) {
+    auto kaddr = [&](int t) __attribute__((always_inline)) { return slot_addr(t) + k_lane; };
+    auto vaddr = [&](int t) __attribute__((always_inline)) { return slot_addr(t) + v_lane; };
+    float mx = w.m;         // exact running max of the kept tiles (tile 0's row max)
+    bool skip_all = false;  // the whole wave drops the tile whose P is in w.p
+    auto body = [&](int j, auto mask_tag) __attribute__((always_inline)) {
+      if (j + kSlots - 1 < nt) load(j + kSlots - 1);
+      if (skip_all)
+        mfma_block<true, false, false>(w, sa, kaddr(j + 1), 0);
+      else
+        mfma_block<true, false>(w, sa, kaddr(j + 1), vaddr(j));
+      if (decltype(mask_tag)::value) mask_tail(sa);
+      float v = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v = fmaxf(v, sa[kb][e]);
+      v = pair_max(v);
+      const bool skip = !row_valid || (v - mx) * w.c < a.skip_log2;
+      skip_all = __builtin_amdgcn_ballot_w64(!skip) == 0;
+      skipped += skip_all ? 1u : 0u;
+      if (!skip) mx = fmaxf(mx, v);
+      const bool need = !skip && v > w.mt;  // a dropped tile never raises the maximum
+      if (__builtin_amdgcn_ballot_w64(need)) raise_max<true>(w, need, v);
+      if (!skip_all) valu_block_off(w, sa, skip ? -INFINITY : w.nmc);
+      loads_done();
+      __syncthreads();
+    };
+    valu_block<false>(w, sa);  // tile 0 is always kept
+    for (int j = 0; j < nt - 2; ++j) body(j, F{});
+    if (nt >= 2) body(nt - 2, T{});
+    if (!skip_all) mfma_block<false, false>(w, sa, 0, vaddr(nt - 1));
+    loads_done();
+    __syncthreads();
+  };
+
   // Fast pass: waves 0-3 take the interleaved steps and waves 4-7 the MFMA-first ones.
   // A workgroup's waves are placed on the SIMDs in turn, so waves w and w + 4 share a
   // SIMD: while one runs the exp2 work that the interleaved form packs into its QK half,
@@ -715,7 +778,18 @@ attn_fwd_kernel(AttnArgs a) {
   // interleaved A/Bs, the same output bits).  The checked pass pairs its waves the same
   // way and takes the multiply-add path for either kind of K (c = 1 for prescaled K):
   // the rare raise of the running max needs registers the kPre path would spill.
-  if constexpr (!kCheck) {
+  if constexpr (kSkip) {
+    skip_steps();
+    __shared__ uint32_t wave_skipped[kWaves];
+    if (lane == 0) wave_skipped[wave] = skipped;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t total = 0;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) total += wave_skipped[i];
+      a.wg_checked[wg] = (int)total;
+    }
+  } else if constexpr (!kCheck) {
     if (prescaled) {
       if (wave >= kWaves / 2)
         mfma_first_steps(T{});

@@ -269,10 +269,14 @@ h3_status do_kv_pack(const void* k, const void* v, const void* w_k, int64_t w_he
 }
 
 // ---------------------------------------------------------------- stage 2: attention
+// skip_threshold > 0: dense attention with Skip-Softmax (one launch over every
+// workgroup, keys never split: the rule walks each row's tiles from the first).
 h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head_stride,
                          float eps, const h3_rope* rope, float softmax_scale,
                          const h3_shape* shp, void* workspace, size_t ws_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, float skip_threshold = 0.0f) {
+  if (!(skip_threshold >= 0.0f && skip_threshold < 1.0f)) return H3_ERR_SHAPE;
+  const bool skip = skip_threshold > 0.0f;
   int64_t max_valid = 0;
   H3_TRY(check_shape(shp, &max_valid));
   if (!q || !o) return H3_ERR_NULL;
@@ -294,7 +298,7 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
   float* part_ml = reinterpret_cast<float*>(after_images + flags_bytes(shp) + part_o_bytes(shp));
   for (int b = 0; b < shp->batch; ++b) {
     const char* ws = static_cast<const char*>(workspace) + b * per_batch;
-    const int splits = attn_splits(shp, shp->seq_valid[b]);
+    const int splits = skip ? 1 : attn_splits(shp, shp->seq_valid[b]);
     AttnArgs aa{};
     aa.wg_checked = flags + (size_t)b * kMaxSplits * attn_workgroups(shp);
     aa.splits = splits;
@@ -315,7 +319,16 @@ h3_status do_attn_packed(const void* q, void* o, const void* w_q, int64_t w_head
     aa.w_head_stride = w_head_stride;
     aa.eps = eps;
     aa.rope = ra;
+    aa.skip_log2 = skip ? std::log2(skip_threshold) : -INFINITY;
     const unsigned blocks = (unsigned)((int64_t)H * m_tiles * splits);
+    if (skip) {
+      if (norm)
+        attn_fwd_kernel<true, true, true><<<blocks, attn::kThreads, 0, stream>>>(aa);
+      else
+        attn_fwd_kernel<false, true, true><<<blocks, attn::kThreads, 0, stream>>>(aa);
+      H3_TRY(launched());
+      continue;
+    }
     // fast pass, then the checked pass for the workgroups the fast pass flagged
     if (norm) {
       attn_fwd_kernel<true, false><<<blocks, attn::kThreads, 0, stream>>>(aa);
@@ -590,6 +603,35 @@ h3_status h3_attn_layer(const void* q, const void* k, const void* v, void* o,
                     workspace_bytes_, stream));
   return do_attn_packed(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape, workspace,
                         workspace_bytes_, stream);
+}
+
+h3_status h3_attn_varlen_skip(const void* q, const void* k, const void* v, void* o,
+                              float softmax_scale, float skip_threshold, const h3_shape* shape,
+                              void* workspace, size_t workspace_bytes_, hipStream_t stream) {
+  if (!q || !o) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  if (!(skip_threshold > 0.0f && skip_threshold < 1.0f)) return H3_ERR_SHAPE;
+  H3_TRY(do_kv_pack(k, v, nullptr, 0, 0.0f, nullptr, softmax_scale, shape, workspace,
+                    workspace_bytes_, stream));
+  return do_attn_packed(q, o, nullptr, 0, 0.0f, nullptr, softmax_scale, shape, workspace,
+                        workspace_bytes_, stream, skip_threshold);
+}
+
+h3_status h3_attn_layer_skip(const void* q, const void* k, const void* v, void* o,
+                             const void* w_q, const void* w_k, int64_t w_head_stride, float eps,
+                             const h3_rope* rope, float softmax_scale, float skip_threshold,
+                             const h3_shape* shape, void* workspace, size_t workspace_bytes_,
+                             hipStream_t stream) {
+  if (!q || !o || !w_q || !w_k) return H3_ERR_NULL;
+  if (!aligned16(q) || !aligned16(o)) return H3_ERR_ALIGN;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return H3_ERR_SHAPE;
+  if (!(skip_threshold > 0.0f && skip_threshold < 1.0f)) return H3_ERR_SHAPE;
+  H3_TRY(check_weights(w_q, w_k, w_head_stride));
+  H3_TRY(do_kv_pack(k, v, w_k, w_head_stride, eps, rope, softmax_scale, shape, workspace,
+                    workspace_bytes_, stream));
+  return do_attn_packed(q, o, w_q, w_head_stride, eps, rope, softmax_scale, shape, workspace,
+                        workspace_bytes_, stream, skip_threshold);
 }
 
 size_t h3_attn_layer_noalloc_max_workspace(void) { return kScratchBytes; }

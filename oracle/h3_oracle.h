@@ -145,6 +145,24 @@ int h3o_attn_layer_fp8(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        double skip_threshold, const int64_t* rows, int64_t n_rows, int threads,
                        double* out, double* wmax);
 
+/* ---- Dense attention with Skip-Softmax (the "Skip-Softmax-only" control): see
+ * h3_oracle_skip.cpp.  Same layouts and row semantics as h3o_attn_varlen; the keys are
+ * walked in tiles of p_tile keys and tile t >= 1 is dropped for a row when
+ * exp(tile max - running max of the kept tiles) < skip_threshold; the row is a softmax
+ * over the kept keys.  wmax (optional, [n_rows][heads]): each row's largest normalised
+ * weight.  The layer form applies the fp64 prologue (h3o_prologue) to Q and K first. */
+int h3o_attn_varlen_skip(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         int64_t seq_buf, int64_t n_valid, int64_t heads, int64_t d,
+                         int64_t row_stride, double scale, int64_t p_tile,
+                         double skip_threshold, const int64_t* rows, int64_t n_rows,
+                         int threads, double* out, double* wmax);
+int h3o_attn_layer_skip(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        int64_t seq_buf, int64_t n_valid, int64_t heads, int64_t d,
+                        int64_t row_stride, const uint16_t* w_q, const uint16_t* w_k,
+                        int64_t w_head_stride, double eps, const h3o_rope* rope, double scale,
+                        int64_t p_tile, double skip_threshold, const int64_t* rows,
+                        int64_t n_rows, int threads, double* out, double* wmax);
+
 /* ---- DiT block steps around attention: see h3_oracle_block.cpp for the reading. */
 
 /* One sequence of seq_buf rows of `hidden` channels: for rows t < n_valid,

@@ -17,7 +17,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "h3_oracle.cpp"), os.path.join(_HERE, "h3_oracle_fp8.cpp"),
-         os.path.join(_HERE, "h3_oracle_block.cpp")]
+         os.path.join(_HERE, "h3_oracle_block.cpp"), os.path.join(_HERE, "h3_oracle_skip.cpp")]
 _LIB = os.path.join(_HERE, "libh3oracle.so")
 
 # Plain -O3 (vectorises the independent per-key / per-channel loops); no
@@ -98,6 +98,12 @@ def lib():
         _lib.h3o_attn_layer_fp8.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, I64, D,
                                             ctypes.POINTER(Rope), D, I64, D, P, I64, I, P, P]
         _lib.h3o_attn_layer_fp8.restype = I
+        _lib.h3o_attn_varlen_skip.argtypes = [P, P, P, I64, I64, I64, I64, I64, D, I64, D,
+                                              P, I64, I, P, P]
+        _lib.h3o_attn_varlen_skip.restype = I
+        _lib.h3o_attn_layer_skip.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P, I64, D,
+                                             ctypes.POINTER(Rope), D, I64, D, P, I64, I, P, P]
+        _lib.h3o_attn_layer_skip.restype = I
         _lib.h3o_residual_norm_modulate.argtypes = [P, P, P, P, P, I64, I64, I64, D, P, P]
         _lib.h3o_residual_norm_modulate.restype = I
     return _lib
@@ -286,6 +292,49 @@ def attn_layer_fp8(q_bits, k_bits, v_bits, n_valid: int, wq_bits, wk_bits, eps: 
                                     rows.size, threads or default_threads(), _ptr(out),
                                     _ptr(wmax)),
            "attn_layer_fp8")
+    return (out, wmax) if with_wmax else out
+
+
+# ---- dense attention with Skip-Softmax (the "Skip-Softmax-only" control)
+
+SKIP_P_TILE = 64  # keys per tile of the Skip-Softmax decision
+
+
+def attn_varlen_skip(q_bits, k_bits, v_bits, n_valid: int, scale: float, rows,
+                     skip_threshold: float, threads: int | None = None,
+                     p_tile: int = SKIP_P_TILE, with_wmax: bool = False):
+    """Dense attention over bf16 [S, H, D] buffers (Q/K already prepared) with tiles of
+    ``p_tile`` keys dropped per row by the Skip-Softmax rule -> [R, H, D] (and, with
+    ``with_wmax``, each row's largest normalised weight [R, H])."""
+    q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
+    S, H, D = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), dtype=np.float64)
+    wmax = np.empty((rows.size, H), dtype=np.float64)
+    _check(lib().h3o_attn_varlen_skip(_ptr(q), _ptr(k), _ptr(v), S, int(n_valid), H, D, H * D,
+                                      float(scale), int(p_tile), float(skip_threshold),
+                                      _ptr(rows), rows.size, threads or default_threads(),
+                                      _ptr(out), _ptr(wmax)), "attn_varlen_skip")
+    return (out, wmax) if with_wmax else out
+
+
+def attn_layer_skip(q_bits, k_bits, v_bits, n_valid: int, wq_bits, wk_bits, eps: float,
+                    rope: Rope, scale: float, rows, skip_threshold: float,
+                    w_head_stride: int = 0, threads: int | None = None,
+                    p_tile: int = SKIP_P_TILE, with_wmax: bool = False):
+    """fp64 RMSNorm + RoPE, then attention_varlen_skip's attention."""
+    q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
+    wq, wk = _u16(wq_bits), _u16(wk_bits)
+    S, H, D = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, H, D), dtype=np.float64)
+    wmax = np.empty((rows.size, H), dtype=np.float64)
+    _check(lib().h3o_attn_layer_skip(_ptr(q), _ptr(k), _ptr(v), S, int(n_valid), H, D, H * D,
+                                     _ptr(wq), _ptr(wk), int(w_head_stride), float(eps),
+                                     ctypes.byref(rope), float(scale), int(p_tile),
+                                     float(skip_threshold), _ptr(rows), rows.size,
+                                     threads or default_threads(), _ptr(out), _ptr(wmax)),
+           "attn_layer_skip")
     return (out, wmax) if with_wmax else out
 
 
