@@ -317,9 +317,9 @@ def main() -> int:
         B.attn_layer(d["q"], d["k"], d["v"], d["w_q"], d["w_k"], n, w.eps, rope, scale,
                      out=out, workspace=ws)
 
-    def launches(name, fn, nbytes=None, flop=None):
+    def launches(name, fn, nbytes=None, flop=None, sources=KERNEL_SOURCES):
         """One untimed call, then args.steps calls bracketed by HIP events on the launch
-        stream; prints one JSON line of their average time."""
+        stream; returns the record of their average time (source_hash: of `sources`)."""
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -332,7 +332,7 @@ def main() -> int:
         ms = e0.elapsed_time(e1) / args.steps
         rec = {"only": name, "workload": w.name, "launches_timed": args.steps,
                "launches_total": args.steps + 1, "ms_per_launch": round(ms, 4),
-               "sclk_mhz": sclk_mhz(), "source_hash": source_hash(FP8_KERNEL_SOURCES)}
+               "sclk_mhz": sclk_mhz(), "source_hash": source_hash(sources)}
         if flop is not None:
             rec["tflops"] = round(flop / ms / 1e9, 2)
             rec["frac_bf16_peak"] = round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
@@ -356,7 +356,7 @@ def main() -> int:
         rec = launches("attn_fp8", lambda: B.attn_packed_fp8(d["q"], ws8, n, scale,
                                                              w_q=d["w_q"], eps=w.eps,
                                                              rope=rope, out=out),
-                       flop=w.flops)
+                       flop=w.flops, sources=FP8_KERNEL_SOURCES)
         rec["frac_fp8_peak"] = round(rec["tflops"] / PEAK_FP8_TFLOPS, 4)
         print(json.dumps(rec), flush=True)
         return 0
