@@ -311,6 +311,13 @@ struct Wave {
 // 8 waves x 32 query rows per workgroup, two waves per SIMD; per 64-key tile and wave:
 // 4 QK products, the softmax of the previous tile, 4 PV products and the row-sum
 // product.  One barrier per tile; tiles are copied global -> LDS into a 3-slot ring.
+// Waves 0-3 interleave the softmax of tile j with the QK products of tile j+1; their
+// SIMD partners (waves 4-7) run the same arithmetic MFMA-first: the step's 9 products
+// back to back, then the max and P codes of the new tile as one VALU block.  Two
+// interleaving waves on a SIMD want the VALU at the same time and the younger one waits
+// (the older wave wins issue); the MFMA-first partner takes the matrix pipe while the
+// interleaving wave runs its softmax.  Same operations in the same order per row, so
+// the same output bits.
 template <bool kFusedQ, bool kSkip>
 __global__ __launch_bounds__(fp8::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attn_fp8_kernel(Fp8AttnArgs a) {
@@ -579,6 +586,92 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     if (t < nt) load(t);
   loads_done();
   __syncthreads();
+
+  // MFMA-first step for tile j: the QK products of tile j+1 and the PV and row-sum
+  // products of tile j back to back (operands read two products ahead), then the max
+  // and the P codes of tile j+1 (kLast: no tile j+1; kMaskNext: tile j+1 is the last).
+  // One score set: tile j+1's scores become P codes before the next QK overwrites them.
+  auto mf_step = [&](f32x16* s, float* cbv, int j, auto last_tag, auto mask_next_tag)
+      __attribute__((always_inline)) {
+    constexpr bool kLast = decltype(last_tag)::value;
+    constexpr bool kMaskNext = decltype(mask_next_tag)::value;
+    using MN = std::integral_constant<bool, kMaskNext>;
+    if (j + kSlots - 1 < nt) load(j + kSlots - 1);
+    const bool run = !(kSkip && w.skip_all);
+    if (!run) ++w.skipped;
+    {
+      // operand i: QK (i < 4: key half i & 1, channel half i >> 1), PV (4 <= i < 8:
+      // channel block i - 4)
+      const uint32_t kb0 = slot_addr(j + 1) + k_lane;
+      const uint32_t vb0 = slot_addr(j) + v_lane;
+      constexpr int i0 = kLast ? 4 : 0;
+      i32x8 op[8];
+      auto rd = [&](int i) __attribute__((always_inline)) {
+        if (i < 4)
+          op[i] = read32(kb0, (i & 1) * 32 * kKPitch + (i >> 1) * 64);
+        else if (i < 8)
+          op[i] = read32(vb0, (i - 4) * 32 * kVPitch);
+      };
+      if (i0 < 4 || run) {
+        rd(i0);
+        rd(i0 + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = i0; i < 9; ++i) {
+        if (i < 4) {
+          s[i & 1] = fp8::mfma8(op[i], w.q[i >> 1], (i >> 1) ? s[i & 1] : f32x16{});
+          if (i + 2 < 4 || run) rd(i + 2);
+        } else if (run) {
+          if (i < 8) {
+            w.o[i - 4] = fp8::mfma8(op[i], w.p, w.o[i - 4]);
+            rd(i + 2);
+          } else {
+            w.l = fp8::mfma_ones(ones, w.p, w.l);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (!kLast) {
+      block_c(j + 1, cbv);
+      update_max(s, cbv, MN{});
+      if (!(kSkip && w.skip_all)) {
+        softmax_half(s[0], cbv, 0, MN{});
+        softmax_half(s[1], cbv, 1, MN{});
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    loads_done();  // tile j+2 in LDS before the next step
+    __syncthreads();
+  };
+
+  if (wave >= kCopyWaves) {
+    // the empty asm keeps the compiler from hoisting either form's first LDS reads above
+    // the branch (which lengthened their live ranges into a spill)
+    asm volatile("" ::: "memory");
+    f32x16 s1[2];
+    float cbv[4];
+    qk(s1, 0);
+    block_c(0, cbv);
+    auto first = [&](auto mask_tag) __attribute__((always_inline)) {
+      update_max(s1, cbv, mask_tag);
+      if (!(kSkip && w.skip_all)) {
+        softmax_half(s1[0], cbv, 0, mask_tag);
+        softmax_half(s1[1], cbv, 1, mask_tag);
+      }
+    };
+    if (nt == 1) {
+      first(T{});
+      mf_step(s1, cbv, 0, T{}, F{});
+    } else {
+      first(F{});
+      for (int j = 0; j < nt - 2; ++j) mf_step(s1, cbv, j, F{}, F{});
+      mf_step(s1, cbv, nt - 2, F{}, T{});
+      mf_step(s1, cbv, nt - 1, T{}, F{});
+    }
+  } else {
+  asm volatile("" ::: "memory");
   f32x16 sa[2], sb[2];
   float ca[4], cb[4];
   qk(sa, 0);
@@ -609,6 +702,7 @@ attn_fp8_kernel(Fp8AttnArgs a) {
     step(sa, sb, ca, cb, nt - 2, F{}, T{});
     step(sb, sa, cb, ca, nt - 1, T{}, F{});
   }
+  }  // interleaving waves
 
   if (kSkip) {  // wave tiles this workgroup skipped
     __shared__ uint32_t wave_skipped[kWaves];
