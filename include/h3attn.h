@@ -28,6 +28,10 @@
  *  - Rows [N_b, S) of every input may hold anything, NaN included; they never
  *    enter the arithmetic.  Output rows [N_b, S) of an attention call are written
  *    as exact zeros.  N_b = 0 is valid.
+ *  - Valid rows must be finite.  The attention sums are accumulated in fp32 with each
+ *    softmax term at most 2^64 times the row's first-tile maximum term (at most 2^8 on
+ *    the workgroups that fail the fast pass's score bound), so for any length the
+ *    interface accepts (S <= 2^30) no accumulator overflows while max |V| < 2^34.
  *  - All work is enqueued asynchronously on `stream` (NULL: the default stream).
  *    The status reports argument validation and launch errors only; faults on the
  *    device surface at the caller's next synchronisation.  Nothing is allocated
