@@ -19,7 +19,9 @@ inputs already resident in HBM.  Prints one JSON line:
              and its pre-pass; reported beside the bf16 headline, never as `value`.
              fp8.skip_softmax: the same step with Skip-Softmax (threshold 0.01) on these
              inputs and on frame-local inputs of the same shape, with the share of wave
-             tiles skipped and the dense bf16 / dense FP8 times on those inputs
+             tiles skipped and the dense bf16 / dense FP8 times on those inputs, and a
+             threshold sweep on the frame-local inputs (time, share skipped, distance of
+             the output from dense FP8)
   skip_softmax_only  the Skip-Softmax-only control (h3_attn_layer_skip: dense bf16 with
              tile skipping, threshold 0.01) on these and on the frame-local inputs
   per_workload  every workload size: h3_attn_layer and h3_attn_varlen TFLOP/s (median and
@@ -60,6 +62,7 @@ METRIC = "attention TFLOP/s + % bf16 MFMA peak, 42 heads x 58,758 valid tokens, 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense FP8 MFMA, published
 SKIP_LAMBDA = 0.01             # Skip-Softmax threshold reported by the bench
+SKIP_SWEEP = (0.01, 0.05, 0.1, 0.2)  # thresholds of the speed / accuracy sweep
 LOCAL_ALPHA = 12.0             # strength of the frame-local input structure
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = ("long_sequence_attention_h3_amd/csrc/attention.hpp",
@@ -529,7 +532,30 @@ def main() -> int:
                                                w.eps, rope, scale, out=out, workspace=ws),
                           args.steps)
     dense_local = skip_run(dl, 0.0)
-    skip_local = skip_run(dl, SKIP_LAMBDA)
+    dense_out = out8[0, :w.n_valid].float()  # dense FP8 on the frame-local inputs
+
+    def distance():
+        """Relative L2 and max |difference| of the last FP8 output from dense FP8."""
+        diff = out8[0, :w.n_valid].float() - dense_out
+        return (round((diff.norm() / dense_out.norm()).item(), 5),
+                round(diff.abs().max().item(), 5))
+
+    # the threshold trades accuracy for speed: a sweep on the same inputs, each point with
+    # its output's distance from dense FP8
+    sweep = []
+    skip_local = None
+    for lam in SKIP_SWEEP:
+        r = skip_run(dl, lam)
+        if lam == SKIP_LAMBDA:
+            skip_local = r
+        rel, mx = distance()
+        sweep.append({"threshold": lam, "ms_per_step": r["ms_per_step"],
+                      "speedup_over_fp8_dense": round(dense_local["ms_per_step"] /
+                                                      r["ms_per_step"], 3),
+                      "wave_tiles_skipped": r["wave_tiles_skipped"],
+                      "rel_l2_vs_fp8_dense": rel, "max_abs_vs_fp8_dense": mx})
+    del dense_out
+    assert skip_local is not None, "the sweep includes the reported threshold"
     skip["frame_local"] = {
         "inputs": f"workloads.generate_local(alpha={LOCAL_ALPHA}, frame=804): one direction "
                   "per 804-token block on the 16 lowest-frequency RoPE pairs",
@@ -537,7 +563,8 @@ def main() -> int:
         "fp8_skip": skip_local,
         "speedup_skip_over_fp8_dense": round(dense_local["ms_per_step"] /
                                              skip_local["ms_per_step"], 3),
-        "speedup_skip_over_bf16_dense": round(ms_bf16_local / skip_local["ms_per_step"], 3)}
+        "speedup_skip_over_bf16_dense": round(ms_bf16_local / skip_local["ms_per_step"], 3),
+        "threshold_sweep": sweep}
     fp8["skip_softmax"] = skip
     log(f"[bench] skip-softmax {SKIP_LAMBDA}: this workload {skip['this_workload']}; "
         f"frame-local bf16 {ms_bf16_local:.3f} ms, fp8 dense {dense_local['ms_per_step']} ms, "
