@@ -23,7 +23,8 @@ inputs already resident in HBM.  Prints one JSON line:
              threshold sweep on the frame-local inputs (time, share skipped, distance of
              the output from dense FP8)
   skip_softmax_only  the Skip-Softmax-only control (h3_attn_layer_skip: dense bf16 with
-             tile skipping, threshold 0.01) on these and on the frame-local inputs
+             tile skipping, threshold 0.01) on these and on the frame-local inputs, with
+             the same threshold sweep on the frame-local inputs
   per_workload  every workload size: h3_attn_layer and h3_attn_varlen TFLOP/s (median and
              min of 10 calls after 3 warm-up calls), the same for the FP8 calls,
              h3_qk_rmsnorm_rope GB/s, and (unless --no-cpu-baseline) `oracle`: the fp64
@@ -585,10 +586,27 @@ def main() -> int:
                  "rule": skip["rule"] + " (dense bf16, exact running max of the kept tiles)",
                  "this_workload": bf16_skip_run(d, SKIP_LAMBDA),
                  "this_workload_bf16_dense_ms": round(ms_step, 4)}
-    sk_local = bf16_skip_run(dl, SKIP_LAMBDA)
+    # dense bf16 on the frame-local inputs, the reference of the sweep's distances
+    B.attn_layer(dl["q"], dl["k"], dl["v"], dl["w_q"], dl["w_k"], n, w.eps, rope, scale,
+                 out=out, workspace=ws)
+    dense16 = out[0, :w.n_valid].float()
+    sweep16, sk_local = [], None
+    for lam in SKIP_SWEEP:
+        r = bf16_skip_run(dl, lam)
+        if lam == SKIP_LAMBDA:
+            sk_local = r
+        diff = out[0, :w.n_valid].float() - dense16
+        sweep16.append({"threshold": lam, "ms_per_step": r["ms_per_step"],
+                        "speedup_over_bf16_dense": round(ms_bf16_local / r["ms_per_step"], 3),
+                        "wave_tiles_skipped": r["wave_tiles_skipped"],
+                        "rel_l2_vs_bf16_dense": round((diff.norm() / dense16.norm()).item(), 5),
+                        "max_abs_vs_bf16_dense": round(diff.abs().max().item(), 5)})
+        del diff
+    del dense16
     skip_only["frame_local"] = {"bf16_dense_ms": round(ms_bf16_local, 4), "bf16_skip": sk_local,
                                 "speedup_over_bf16_dense": round(ms_bf16_local /
-                                                                 sk_local["ms_per_step"], 3)}
+                                                                 sk_local["ms_per_step"], 3),
+                                "threshold_sweep": sweep16}
     log(f"[bench] skip-softmax-only (bf16) {SKIP_LAMBDA}: this workload "
         f"{skip_only['this_workload']}; frame-local {sk_local['ms_per_step']} ms "
         f"({100 * sk_local['wave_tiles_skipped']:.1f} % of wave tiles skipped) vs dense "
